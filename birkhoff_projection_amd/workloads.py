@@ -1,0 +1,148 @@
+"""Seeded synthetic workloads for the Birkhoff projection.
+
+This module holds random inputs and storage encodings only -- none of the
+projection's arithmetic -- so that the HIP path and the float64 oracle can be
+fed the very same numbers.  It imports nothing else from the package.
+
+Recipe (every workload): a ``numpy.random.Generator(PCG64(seed))`` draws float64
+standard normals, which are scaled, then rounded to fp32 (round-to-nearest-
+even) and, for bf16 storage, rounded again fp32 -> bf16 (RNE).  Logits use
+``seed``; the upstream gradient dL/dT uses ``seed + 100``.  Matrices are
+row-major and stored back to back, shape [B, n, n].
+
+The distributions follow the pages' experiments ("Accelerating Birkhoff
+Projection for Manifold-Constrained Hyper-Connections", section 5: N(0,1),
+N(0,10^2)) and the benchmark shapes below; no dataset is involved.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional, Tuple
+
+import numpy as np
+
+_CHUNK = 1 << 20  # matrices drawn per generator call (bounds host memory)
+
+
+@dataclass(frozen=True)
+class Workload:
+    key: str
+    title: str
+    B: int
+    n: int
+    io: str                      # storage of logits / T / dT / dH: "f32" or "bf16"
+    logits: Tuple                # recipe, see make_logits
+    upstream: Optional[Tuple]    # recipe for dL/dT, None if forward only
+    passes: str                  # "fwd+bwd" or "fwd"
+    seed: int
+    tol: float = 1e-6
+    max_iter: int = 50
+    sk_cap: int = 10_000         # oracle Sinkhorn cap for the reference
+    extra: dict = field(default_factory=dict)
+
+
+WORKLOADS = {
+    "pr1": Workload(
+        key="pr1", title="4x4 fp32, B=4096, H~N(0,1), dT~N(0,1)",
+        B=4096, n=4, io="f32", logits=("normal", 1.0), upstream=("normal", 1.0),
+        passes="fwd+bwd", seed=1),
+    "hard": Workload(
+        key="hard", title="4x4 fp32, B=1,048,576, H~N(0,s^2), s per matrix from {1,3,5,8}",
+        B=1 << 20, n=4, io="f32", logits=("sigma_mix", (1.0, 3.0, 5.0, 8.0)), upstream=None,
+        passes="fwd", seed=2, max_iter=100, sk_cap=5_000),
+    "train": Workload(
+        key="train", title="4x4 fp32, B=16x4096x32=2,097,152, H~N(0,0.5^2)+2I, dT~N(0,0.1^2)",
+        B=16 * 4096 * 32, n=4, io="f32", logits=("near_identity", 0.5, 2.0),
+        upstream=("normal", 0.1), passes="fwd+bwd", seed=3),
+    "n8": Workload(
+        key="n8", title="8x8 fp32, B=1,048,576, H~N(0,1), dT~N(0,1)",
+        B=1 << 20, n=8, io="f32", logits=("normal", 1.0), upstream=("normal", 1.0),
+        passes="fwd+bwd", seed=4),
+    "bw": Workload(
+        key="bw", title="4x4 bf16 storage, B=16,777,216, H~N(0,1), dT~N(0,1)",
+        B=1 << 24, n=4, io="bf16", logits=("normal", 1.0), upstream=("normal", 1.0),
+        passes="fwd+bwd", seed=5),
+}
+
+
+def _draw(recipe: Tuple, B: int, n: int, seed: int) -> np.ndarray:
+    """fp32 [B, n, n] values for a recipe (scaling done in float64, then rounded)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    kind = recipe[0]
+    out = np.empty((B, n, n), dtype=np.float32)
+    if kind == "normal":
+        sigma = float(recipe[1])
+        for s in range(0, B, _CHUNK):
+            e = min(B, s + _CHUNK)
+            out[s:e] = sigma * rng.standard_normal((e - s, n, n))
+    elif kind == "sigma_mix":
+        sigmas = np.asarray(recipe[1], dtype=np.float64)
+        idx = rng.integers(0, len(sigmas), size=B)          # sigma index first
+        for s in range(0, B, _CHUNK):
+            e = min(B, s + _CHUNK)
+            z = rng.standard_normal((e - s, n, n))
+            out[s:e] = sigmas[idx[s:e]][:, None, None] * z
+    elif kind == "near_identity":
+        sigma, diag = float(recipe[1]), float(recipe[2])
+        eye = np.eye(n) * diag
+        for s in range(0, B, _CHUNK):
+            e = min(B, s + _CHUNK)
+            out[s:e] = sigma * rng.standard_normal((e - s, n, n)) + eye
+    else:
+        raise ValueError("unknown recipe %r" % (kind,))
+    return out
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (round to nearest, ties to even); returns uint16 bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    r = ((u + bias) >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        r[nan] = np.uint16(0x7FC0)
+    return r
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact decode of bf16 bit patterns to fp32."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def make_logits(w: Workload, B: Optional[int] = None, seed: Optional[int] = None) -> np.ndarray:
+    """Logits H~ for workload w: fp32 [B, n, n], or uint16 bf16 bits when w.io == 'bf16'."""
+    B = w.B if B is None else int(B)
+    x = _draw(w.logits, B, w.n, w.seed if seed is None else seed)
+    return f32_to_bf16_bits(x) if w.io == "bf16" else x
+
+
+def make_upstream(w: Workload, B: Optional[int] = None, seed: Optional[int] = None) -> np.ndarray:
+    """Upstream gradient dL/dT for workload w (same storage rule as the logits)."""
+    if w.upstream is None:
+        raise ValueError("workload %s is forward only" % w.key)
+    B = w.B if B is None else int(B)
+    x = _draw(w.upstream, B, w.n, (w.seed + 100) if seed is None else seed)
+    return f32_to_bf16_bits(x) if w.io == "bf16" else x
+
+
+def decode_f64(x: np.ndarray) -> np.ndarray:
+    """Exact float64 view of stored inputs/outputs (fp32 array or bf16 bit patterns)."""
+    if x.dtype == np.uint16:
+        return bf16_bits_to_f32(x).astype(np.float64)
+    return np.asarray(x, dtype=np.float64)
+
+
+def bytes_per_projection(n: int, io: str, passes: str) -> int:
+    """Algorithmic HBM bytes per projection: each input read once, each output written once.
+
+    fwd: logits + T (n*n elements of the storage type each) + dual (n fp32);
+    bwd: logits + dual + dT + dH.
+    """
+    s = 2 if io == "bf16" else 4
+    fwd = 2 * n * n * s + 4 * n
+    bwd = 3 * n * n * s + 4 * n
+    if passes == "fwd":
+        return fwd
+    if passes == "bwd":
+        return bwd
+    return fwd + bwd

@@ -1,0 +1,487 @@
+/*
+ * oracle.c -- float64 CPU oracle for the KL projection onto the Birkhoff
+ * polytope, its implicit-differentiation backward pass and the fixed-sweep
+ * Sinkhorn-Knopp baseline.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark load this library.  The product path
+ * (the HIP library and its Python binding) never calls, links or includes it,
+ * and this file includes nothing from the product path.
+ *
+ * Sources (cited by title and section / equation only):
+ *   [P]  "Accelerating Birkhoff Projection for Manifold-Constrained
+ *        Hyper-Connections", sections 2.2-4.2, equations (1)-(13).
+ *   [B]  the author's blog post "浅谈 DeepSeek mHC 一种可能的加速方案：
+ *        小矩阵遇上牛顿法" ("small matrices meet Newton's method"),
+ *        section 2.2 (step-size rule and Sinkhorn fallback).
+ *
+ * Conventions.  H is the n x n logit matrix (the pages' R = -M), so the
+ * projected matrix is T = proj_KL(exp(H)).  With eta = 1 and a = b = 1
+ * ([P] end of section 2.3) the dual pair (alpha, beta) recovers
+ * T_ij = exp(alpha_i + beta_j + H_ij) (eq 4).  beta is always reported in the
+ * gauge beta_n = 0 ([P] section 3.1).  Every matrix is row-major, matrices
+ * are stored back to back ([B, n, n]).
+ *
+ * Precision.  Everything is IEEE double; no -ffast-math.  Plain libm exp,
+ * log, expm1 and log1p.
+ *
+ * Parity pins.  Every exported function is pinned by tests that do not call
+ * this code for the expected value: the n = 2 closed form, exactly known
+ * fixed points (doubly stochastic inputs with row/column shifts), rank-one
+ * inputs, a constrained primal solver for eq (1), a library minimiser for
+ * eq (8), finite differences and unrolled autograd for eq (13), and hand
+ * computed Sinkhorn sweeps for eq (2).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_NMAX 16
+
+/* ------------------------------------------------------------------ */
+/* small helpers                                                        */
+/* ------------------------------------------------------------------ */
+
+/* log(sum_k exp(v[k*s])), k < m, shifted by the maximum.  NaN propagates. */
+static double lse(const double *v, int m, int s)
+{
+    double mx = -INFINITY;
+    int nan = 0;
+    for (int k = 0; k < m; ++k) {
+        double x = v[k * s];
+        if (x != x) nan = 1;
+        else if (x > mx) mx = x;
+    }
+    if (nan) return NAN;
+    if (mx == -INFINITY || mx == INFINITY) return mx;
+    double acc = 0.0;
+    for (int k = 0; k < m; ++k) acc += exp(v[k * s] - mx);
+    return mx + log(acc);
+}
+
+/* eq (5) with M = -H, eta = 1, a = 1:  alpha_i = -log sum_j exp(beta_j + H_ij) */
+static void alpha_of_beta(const double *H, int n, const double *beta, double *alpha)
+{
+    double u[ORACLE_NMAX];
+    for (int i = 0; i < n; ++i) {
+        for (int j = 0; j < n; ++j) u[j] = H[i * n + j] + beta[j];
+        alpha[i] = -lse(u, n, 1);
+    }
+}
+
+/* eq (6) with M = -H, eta = 1, b = 1:  beta_j = -log sum_i exp(alpha_i + H_ij) */
+static void beta_of_alpha(const double *H, int n, const double *alpha, double *beta)
+{
+    double u[ORACLE_NMAX];
+    for (int j = 0; j < n; ++j) {
+        for (int i = 0; i < n; ++i) u[i] = H[i * n + j] + alpha[i];
+        beta[j] = -lse(u, n, 1);
+    }
+}
+
+/* primal recovery after eq (4):  T_ij = exp(alpha_i + beta_j + H_ij) */
+static void primal(const double *H, int n, const double *alpha, const double *beta, double *T)
+{
+    for (int i = 0; i < n; ++i)
+        for (int j = 0; j < n; ++j) T[i * n + j] = exp(alpha[i] + beta[j] + H[i * n + j]);
+}
+
+/* max over rows and columns of |sum - 1| (distance to the marginals of B_n) */
+static double marginal_residual(const double *T, int n)
+{
+    double r = 0.0;
+    for (int i = 0; i < n; ++i) {
+        double s = 0.0;
+        for (int j = 0; j < n; ++j) s += T[i * n + j];
+        double e = fabs(s - 1.0);
+        if (!(e <= r)) r = e; /* NaN propagates */
+    }
+    for (int j = 0; j < n; ++j) {
+        double s = 0.0;
+        for (int i = 0; i < n; ++i) s += T[i * n + j];
+        double e = fabs(s - 1.0);
+        if (!(e <= r)) r = e;
+    }
+    return r;
+}
+
+static double max_abs_diff(const double *a, const double *b, int len)
+{
+    double r = 0.0;
+    for (int k = 0; k < len; ++k) {
+        double e = fabs(a[k] - b[k]);
+        if (!(e <= r)) r = e;
+    }
+    return r;
+}
+
+/* Solve A x = b in place (A is m x m row-major, overwritten; x returned in b)
+ * by Gaussian elimination with partial pivoting.  Returns 0, or -1 when a
+ * pivot is zero or not finite. */
+static int solve_gepp(double *A, double *b, int m)
+{
+    for (int k = 0; k < m; ++k) {
+        int p = k;
+        double best = fabs(A[k * m + k]);
+        for (int r = k + 1; r < m; ++r) {
+            double v = fabs(A[r * m + k]);
+            if (v > best) { best = v; p = r; }
+        }
+        if (!(best > 0.0) || !isfinite(best)) return -1;
+        if (p != k) {
+            for (int c = 0; c < m; ++c) {
+                double t = A[k * m + c]; A[k * m + c] = A[p * m + c]; A[p * m + c] = t;
+            }
+            double t = b[k]; b[k] = b[p]; b[p] = t;
+        }
+        for (int r = k + 1; r < m; ++r) {
+            double f = A[r * m + k] / A[k * m + k];
+            if (f == 0.0) continue;
+            for (int c = k; c < m; ++c) A[r * m + c] -= f * A[k * m + c];
+            b[r] -= f * b[k];
+        }
+    }
+    for (int k = m - 1; k >= 0; --k) {
+        double s = b[k];
+        for (int c = k + 1; c < m; ++c) s -= A[k * m + c] * b[c];
+        b[k] = s / A[k * m + k];
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Sinkhorn-Knopp in log form ([P] eq (2), as the BCA of eq (7))        */
+/* ------------------------------------------------------------------ */
+
+/* Sweeps from beta = 0 (v^(0) = 1) until the marginal residual of
+ * T = exp(alpha + beta + H) is <= tol, at most cap sweeps.  One sweep is the
+ * row update (eq 5) followed by the column update (eq 6).  Returns the number
+ * of sweeps; *conv = 1 when the tolerance was met. */
+static int sk_to_tol_one(const double *H, int n, double tol, int cap,
+                         double *T, double *beta_out, int *conv)
+{
+    double alpha[ORACLE_NMAX], beta[ORACLE_NMAX];
+    for (int j = 0; j < n; ++j) beta[j] = 0.0;
+    *conv = 0;
+    int k = 0;
+    while (k < cap) {
+        ++k;
+        alpha_of_beta(H, n, beta, alpha);
+        beta_of_alpha(H, n, alpha, beta);
+        primal(H, n, alpha, beta, T);
+        if (marginal_residual(T, n) <= tol) { *conv = 1; break; }
+    }
+    if (k == 0) { /* cap == 0: report the un-scaled starting point */
+        alpha_of_beta(H, n, beta, alpha);
+        primal(H, n, alpha, beta, T);
+    }
+    for (int j = 0; j < n; ++j) beta_out[j] = beta[j] - beta[n - 1];
+    return k;
+}
+
+/* Exactly K sweeps from beta = 0, then T = diag(u) A diag(v)
+ * (after K sweeps the column sums are exact; rows carry the error). */
+static void sk_fixed_one(const double *H, int n, int K, double *T)
+{
+    double alpha[ORACLE_NMAX], beta[ORACLE_NMAX];
+    for (int j = 0; j < n; ++j) beta[j] = 0.0;
+    for (int k = 0; k < K; ++k) {
+        alpha_of_beta(H, n, beta, alpha);
+        beta_of_alpha(H, n, alpha, beta);
+    }
+    primal(H, n, alpha, beta, T);
+}
+
+/* ------------------------------------------------------------------ */
+/* Newton on the reduced dual ([P] section 3.1, eqs (8)-(9))            */
+/* ------------------------------------------------------------------ */
+
+/* T(beta): row i is Softmax(H_i. + beta), evaluated max-shifted as in eq (10);
+ * c_j = sum_i T_ij (eq 11). */
+static void eval_T(const double *H, int n, const double *beta, double *T, double *c)
+{
+    for (int i = 0; i < n; ++i) {
+        double mu = -INFINITY;
+        for (int j = 0; j < n; ++j) {
+            double u = H[i * n + j] + beta[j];
+            if (u > mu) mu = u;
+        }
+        double s = 0.0;
+        for (int j = 0; j < n; ++j) {
+            double e = exp(H[i * n + j] + beta[j] - mu);
+            T[i * n + j] = e;
+            s += e;
+        }
+        for (int j = 0; j < n; ++j) T[i * n + j] /= s;
+    }
+    for (int j = 0; j < n; ++j) {
+        double s = 0.0;
+        for (int i = 0; i < n; ++i) s += T[i * n + j];
+        c[j] = s;
+    }
+}
+
+static double colsum_residual(const double *c, int n)
+{
+    double r = 0.0;
+    for (int j = 0; j < n; ++j) {
+        double e = fabs(c[j] - 1.0);
+        if (!(e <= r)) r = e;
+    }
+    return r;
+}
+
+/* Newton's method for min_x f(x), x = beta_{-n} (eq 8), from x = 0.
+ *   gradient  g = c_{-n} - 1                           (eq 9, a = b = 1)
+ *   Hessian   diag(c_{-n}) - T_{-n}^T T_{-n}           (eq 9, eta = 1)
+ *   step      x+ = x + gamma d,  d = -Hess^{-1} g
+ * Step size ([B] section 2.2): try gamma = 1, 0.5, 0.1, 0.05, 0.01 in turn and
+ * take the first one at which both the objective and the gradient are smaller
+ * than at x (read as f(x + gamma d) < f(x) and ||g(x + gamma d)||_2 < ||g(x)||_2);
+ * when none is taken, do one Sinkhorn-Knopp sweep (eqs 5-7) and re-gauge
+ * beta_n = 0.  The objective difference is evaluated through the exact identity
+ *   f(x + gamma d) - f(x) = sum_i log(sum_j T_ij e^{gamma d_j}) - gamma sum_j d_j,
+ * which follows from f = n + sum_i LSE_i(H_i. + beta) - sum_j beta_j (eq 8 with
+ * eq 5), written with log1p / expm1 (rows of T sum to one).
+ * Stop when every column sum is within tol of 1 (rows are exact by
+ * construction), or after max_iter updates (a trial point is not an update).
+ * Returns the number of updates, or -1 when tol was not reached. */
+static int newton_one(const double *H, int n, double tol, int max_iter,
+                      double *T, double *beta_out)
+{
+    static const double steps[5] = {1.0, 0.5, 0.1, 0.05, 0.01};
+    const int m = n - 1;
+    double beta[ORACLE_NMAX], c[ORACLE_NMAX], g[ORACLE_NMAX], d[ORACLE_NMAX];
+    double hess[ORACLE_NMAX * ORACLE_NMAX];
+    double bt[ORACLE_NMAX], Tt[ORACLE_NMAX * ORACLE_NMAX], ct[ORACLE_NMAX];
+    double alpha[ORACLE_NMAX];
+    for (int j = 0; j < n; ++j) beta[j] = 0.0;
+    eval_T(H, n, beta, T, c);
+    int it = 0, conv = 0;
+    for (;;) {
+        double res = colsum_residual(c, n);
+        if (res != res) break;
+        if (res <= tol) { conv = 1; break; }
+        if (it >= max_iter) break;
+
+        double gn2 = 0.0;
+        for (int j = 0; j < m; ++j) { g[j] = c[j] - 1.0; gn2 += g[j] * g[j]; }
+        for (int j = 0; j < m; ++j)
+            for (int k = 0; k < m; ++k) {
+                double p = 0.0;
+                for (int i = 0; i < n; ++i) p += T[i * n + j] * T[i * n + k];
+                hess[j * m + k] = (j == k ? c[j] : 0.0) - p;
+            }
+        for (int j = 0; j < m; ++j) d[j] = -g[j];
+        int accepted = 0;
+        if (solve_gepp(hess, d, m) == 0) {
+            for (int s = 0; s < 5 && !accepted; ++s) {
+                double gam = steps[s];
+                double df = 0.0;
+                for (int i = 0; i < n; ++i) {
+                    double acc = 0.0;
+                    for (int j = 0; j < m; ++j) acc += T[i * n + j] * expm1(gam * d[j]);
+                    df += log1p(acc);
+                }
+                for (int j = 0; j < m; ++j) df -= gam * d[j];
+                for (int j = 0; j < m; ++j) bt[j] = beta[j] + gam * d[j];
+                bt[m] = 0.0;
+                eval_T(H, n, bt, Tt, ct);
+                double gt2 = 0.0;
+                for (int j = 0; j < m; ++j) gt2 += (ct[j] - 1.0) * (ct[j] - 1.0);
+                if (df < 0.0 && gt2 < gn2) {
+                    accepted = 1;
+                    memcpy(beta, bt, sizeof(double) * n);
+                    memcpy(T, Tt, sizeof(double) * n * n);
+                    memcpy(c, ct, sizeof(double) * n);
+                }
+            }
+        }
+        if (!accepted) {
+            alpha_of_beta(H, n, beta, alpha);
+            beta_of_alpha(H, n, alpha, beta);
+            double sh = beta[m];
+            for (int j = 0; j < n; ++j) beta[j] -= sh;
+            eval_T(H, n, beta, T, c);
+        }
+        ++it;
+    }
+    for (int j = 0; j < n; ++j) beta_out[j] = beta[j];
+    return conv ? it : -1;
+}
+
+/* ------------------------------------------------------------------ */
+/* Implicit-differentiation backward ([P] section 4.1, eq (13))         */
+/* ------------------------------------------------------------------ */
+
+/* dH = d<G, T*>/dH for T* = proj(exp(H)).  eq (13) with eta = 1, a = b = 1:
+ *   Gamma = G o T*, mu_r = Gamma 1, mu_c = (Gamma^T)_{-n} 1,
+ *   Delta = I - T*_{-n}^T T*_{-n},
+ *   w_{-n} = Delta^{-1} (mu_c - T*_{-n}^T mu_r),  w_n = 0,
+ *   D = diag(mu_r - T*_{-n} w_{-n}) T* + T* diag(w) - Gamma   (= dl/dM),
+ * and dH = -D because H = -M ([P] end of section 4.2).  Returns -1 when Delta
+ * is singular (dH is then NaN). */
+static int bwd_one(const double *T, const double *G, int n, double *dH)
+{
+    const int m = n - 1;
+    double gam[ORACLE_NMAX * ORACLE_NMAX], mur[ORACLE_NMAX], rhs[ORACLE_NMAX];
+    double delta[ORACLE_NMAX * ORACLE_NMAX], w[ORACLE_NMAX], v[ORACLE_NMAX];
+    for (int k = 0; k < n * n; ++k) gam[k] = G[k] * T[k];
+    for (int i = 0; i < n; ++i) {
+        double s = 0.0;
+        for (int j = 0; j < n; ++j) s += gam[i * n + j];
+        mur[i] = s;
+    }
+    for (int j = 0; j < m; ++j) {
+        double muc = 0.0, tmu = 0.0;
+        for (int i = 0; i < n; ++i) {
+            muc += gam[i * n + j];
+            tmu += T[i * n + j] * mur[i];
+        }
+        rhs[j] = muc - tmu;
+        for (int k = 0; k < m; ++k) {
+            double p = 0.0;
+            for (int i = 0; i < n; ++i) p += T[i * n + j] * T[i * n + k];
+            delta[j * m + k] = (j == k ? 1.0 : 0.0) - p;
+        }
+    }
+    int rc = solve_gepp(delta, rhs, m);
+    for (int j = 0; j < m; ++j) w[j] = rc == 0 ? rhs[j] : NAN;
+    w[m] = 0.0;
+    for (int i = 0; i < n; ++i) {
+        double s = mur[i];
+        for (int j = 0; j < m; ++j) s -= T[i * n + j] * w[j];
+        v[i] = s;
+    }
+    for (int i = 0; i < n; ++i)
+        for (int j = 0; j < n; ++j) {
+            double Dij = v[i] * T[i * n + j] + T[i * n + j] * w[j] - gam[i * n + j];
+            dH[i * n + j] = -Dij;
+        }
+    return rc;
+}
+
+/* ------------------------------------------------------------------ */
+/* exported entry points                                                */
+/* ------------------------------------------------------------------ */
+
+static int bad_args(int64_t B, int n, const void *p)
+{
+    return B < 0 || n < 2 || n > ORACLE_NMAX || (B > 0 && p == NULL);
+}
+
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+int oracle_nmax(void) { return ORACLE_NMAX; }
+
+/* Sinkhorn-Knopp to a marginal residual <= tol (cap sweeps). */
+int oracle_sinkhorn_tol(const double *H, int64_t B, int n, double tol, int cap,
+                        double *T, double *beta, int32_t *sweeps, int32_t *converged)
+{
+    if (bad_args(B, n, H) || (B > 0 && (!T || !beta || !sweeps || !converged)) || cap < 0)
+        return -1;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t b = 0; b < B; ++b) {
+        int conv = 0;
+        sweeps[b] = sk_to_tol_one(H + b * n * n, n, tol, cap, T + b * n * n, beta + b * n, &conv);
+        converged[b] = conv;
+    }
+    return 0;
+}
+
+/* Exactly K Sinkhorn-Knopp sweeps (the fixed-iteration baseline). */
+int oracle_sinkhorn_k(const double *H, int64_t B, int n, int K, double *T)
+{
+    if (bad_args(B, n, H) || (B > 0 && !T) || K < 0) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < B; ++b) sk_fixed_one(H + b * n * n, n, K, T + b * n * n);
+    return 0;
+}
+
+/* Newton's method on the reduced dual; iters[b] = updates, or -1 if tol not met. */
+int oracle_newton(const double *H, int64_t B, int n, double tol, int max_iter,
+                  double *T, double *beta, int32_t *iters)
+{
+    if (bad_args(B, n, H) || (B > 0 && (!T || !beta || !iters)) || max_iter < 0) return -1;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t b = 0; b < B; ++b)
+        iters[b] = newton_one(H + b * n * n, n, tol, max_iter, T + b * n * n, beta + b * n);
+    return 0;
+}
+
+/* Reference projection (float64):
+ *   1. Sinkhorn-Knopp to residual 1e-13 (at most sk_cap sweeps);
+ *   2. Newton to residual 1e-13 (at most 500 updates) as an independent check;
+ *   3. status 0: Sinkhorn converged and both agree within 1e-12 -> Sinkhorn's T;
+ *      status 1: Sinkhorn hit the cap, Newton converged and one further
+ *                Sinkhorn sweep from Newton's dual moves T by <= 1e-12
+ *                (a fixed-point check) -> Newton's T;
+ *      status < 0: no reference could be certified (T holds the best effort).
+ * beta is reported with beta_n = 0. */
+int oracle_project(const double *H, int64_t B, int n, int sk_cap,
+                   double *T, double *beta, int32_t *status)
+{
+    if (bad_args(B, n, H) || (B > 0 && (!T || !beta || !status)) || sk_cap < 0) return -1;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t b = 0; b < B; ++b) {
+        const double *h = H + b * n * n;
+        double tsk[ORACLE_NMAX * ORACLE_NMAX], tnw[ORACLE_NMAX * ORACLE_NMAX];
+        double bsk[ORACLE_NMAX], bnw[ORACLE_NMAX];
+        int conv = 0;
+        sk_to_tol_one(h, n, 1e-13, sk_cap, tsk, bsk, &conv);
+        int it = newton_one(h, n, 1e-13, 500, tnw, bnw);
+        int st;
+        if (conv) {
+            st = (it >= 0 && max_abs_diff(tsk, tnw, n * n) <= 1e-12) ? 0 : -1;
+            memcpy(T + b * n * n, tsk, sizeof(double) * n * n);
+            memcpy(beta + b * n, bsk, sizeof(double) * n);
+        } else {
+            st = -2;
+            if (it >= 0) {
+                double alpha[ORACLE_NMAX], b1[ORACLE_NMAX], t1[ORACLE_NMAX * ORACLE_NMAX];
+                alpha_of_beta(h, n, bnw, alpha);
+                beta_of_alpha(h, n, alpha, b1);
+                primal(h, n, alpha, b1, t1);
+                if (max_abs_diff(t1, tnw, n * n) <= 1e-12) st = 1;
+            }
+            memcpy(T + b * n * n, tnw, sizeof(double) * n * n);
+            memcpy(beta + b * n, bnw, sizeof(double) * n);
+        }
+        status[b] = st;
+    }
+    return 0;
+}
+
+/* Backward pass by eq (13) at the given projected matrices T (the caller
+ * passes the reference T of oracle_project).  Returns the number of matrices
+ * whose Delta was singular (their dH is NaN), or -1 on bad arguments. */
+int oracle_bwd(const double *T, const double *G, int64_t B, int n, double *dH)
+{
+    if (bad_args(B, n, T) || (B > 0 && (!G || !dH))) return -1;
+    int64_t bad = 0;
+#pragma omp parallel for schedule(static) reduction(+ : bad)
+    for (int64_t b = 0; b < B; ++b)
+        if (bwd_one(T + b * n * n, G + b * n * n, n, dH + b * n * n) != 0) ++bad;
+    return (int)(bad > 0x7fffffff ? 0x7fffffff : bad);
+}
+
+/* Marginal residual max(|rowsum - 1|, |colsum - 1|) of each matrix, summed in
+ * double; used to score a projected output against the constraint of B_n. */
+int oracle_residuals(const double *T, int64_t B, int n, double *res)
+{
+    if (bad_args(B, n, T) || (B > 0 && !res)) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < B; ++b) res[b] = marginal_residual(T + b * n * n, n);
+    return 0;
+}

@@ -1,0 +1,16 @@
+"""Shared pytest configuration.
+
+Markers:
+  gpu  -- needs an MI355X (gfx950) and the built HIP library; run with -m gpu.
+Everything unmarked runs on a CPU-only host.
+"""
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an AMD Instinct MI355X (gfx950) and the built HIP library")

@@ -1,0 +1,62 @@
+"""Plant plausible slips in a copy of the oracle (on the CPU) and check that the
+pins in test_oracle.py catch every one of them.
+
+Each mutant is oracle.c with one textual edit (a flipped sign, a dropped term,
+a transposed index, a lost gauge), compiled to a temporary library and loaded
+by the oracle's Python wrapper through ORACLE_LIB in a child pytest run.
+"""
+import os
+import pathlib
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+ROOT = pathlib.Path(__file__).resolve().parent.parent
+SRC = (ROOT / "oracle" / "oracle.c").read_text()
+
+MUTANTS = {
+    "control_unmutated": ("int oracle_nmax(void) { return ORACLE_NMAX; }", "int oracle_nmax(void) { return ORACLE_NMAX; }"),
+    "bwd_sign": ("dH[i * n + j] = -Dij;", "dH[i * n + j] = Dij;"),
+    "bwd_drop_Tdiagw": ("v[i] * T[i * n + j] + T[i * n + j] * w[j] - gam[i * n + j]",
+                        "v[i] * T[i * n + j] - gam[i * n + j]"),
+    "bwd_muc_transposed": ("muc += gam[i * n + j];", "muc += gam[j * n + i];"),
+    "bwd_delta_sign": ("delta[j * m + k] = (j == k ? 1.0 : 0.0) - p;", "delta[j * m + k] = (j == k ? 1.0 : 0.0) + p;"),
+    "bwd_rhs_sign": ("rhs[j] = muc - tmu;", "rhs[j] = muc + tmu;"),
+    "bwd_v_transposed": ("s -= T[i * n + j] * w[j];", "s -= T[j * n + i] * w[j];"),
+    "colupdate_transposed": ("for (int i = 0; i < n; ++i) u[i] = H[i * n + j] + alpha[i];",
+                             "for (int i = 0; i < n; ++i) u[i] = H[j * n + i] + alpha[i];"),
+    "alpha_sign": ("alpha[i] = -lse(u, n, 1);", "alpha[i] = lse(u, n, 1);"),
+    "primal_beta_sign": ("exp(alpha[i] + beta[j] + H[i * n + j])", "exp(alpha[i] - beta[j] + H[i * n + j])"),
+    "lost_gauge": ("beta_out[j] = beta[j] - beta[n - 1];", "beta_out[j] = beta[j];"),
+    "hessian_sign": ("hess[j * m + k] = (j == k ? c[j] : 0.0) - p;", "hess[j * m + k] = (j == k ? c[j] : 0.0) + p;"),
+    "gradient_sign": ("g[j] = c[j] - 1.0; gn2 += g[j] * g[j];", "g[j] = 1.0 - c[j]; gn2 += g[j] * g[j];"),
+    "linesearch_df_sign": ("for (int j = 0; j < m; ++j) df -= gam * d[j];", "for (int j = 0; j < m; ++j) df += gam * d[j];"),
+    "softmax_no_max_shift_wrong": ("double e = exp(H[i * n + j] + beta[j] - mu);", "double e = exp(H[i * n + j] - beta[j] - mu);"),
+}
+
+
+def _run_mutant(name, tmp):
+    old, new = MUTANTS[name]
+    assert SRC.count(old) == 1, "mutation anchor for %s not unique/found" % name
+    src = tmp / ("%s.c" % name)
+    lib = tmp / ("%s.so" % name)
+    src.write_text(SRC.replace(old, new))
+    subprocess.run(["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", str(src), "-o", str(lib), "-lm"],
+                   check=True)
+    env = dict(os.environ, ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        str(ROOT / "tests" / "test_oracle.py")],
+                       cwd=str(ROOT), env=env, capture_output=True, text=True, timeout=600)
+    return name, r.returncode, r.stdout[-400:]
+
+
+def test_every_planted_slip_is_caught(tmp_path):
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        results = list(ex.map(lambda k: _run_mutant(k, tmp_path), sorted(MUTANTS)))
+    by_name = {n: (rc, out) for n, rc, out in results}
+    # the unmutated control must pass, otherwise a failure says nothing about the pins
+    assert by_name.pop("control_unmutated")[0] == 0
+    survived = [(n, out) for n, (rc, out) in by_name.items() if rc == 0]
+    assert not survived, "mutants not caught by the oracle pins: %r" % survived
