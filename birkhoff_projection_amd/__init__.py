@@ -1,1 +1,289 @@
+"""MI355X-native batched KL projection onto the Birkhoff polytope (mHC).
 
+Thin Python binding over libbirkhoff.so (C ABI in include/birkhoff.h).  The
+functions below carry the ABI's names and only marshal arguments: they check
+shapes, dtypes, devices and contiguity of torch tensors, pass raw device
+pointers and torch's current HIP stream, and turn error codes into
+exceptions.  Every step of the computation runs in the HIP kernels; there is
+no CPU or PyTorch fallback.  If the library is not built, every call raises.
+
+    import torch, birkhoff_projection_amd as bp
+    H = torch.randn(4096, 4, 4, device="cuda")
+    T, dual = bp.project(H)                      # forward, allocating outputs
+    T = bp.BirkhoffProjection.apply(H)           # autograd: backward by eq (13)
+"""
+from __future__ import annotations
+
+import ctypes
+import pathlib
+from typing import Optional
+
+__all__ = [
+    "BirkhoffError", "library_path", "load_library",
+    "birkhoff_fwd", "birkhoff_fwd_ex", "birkhoff_bwd", "sinkhorn_fwd",
+    "birkhoff_fwd_bf16", "birkhoff_bwd_bf16", "birkhoff_strerror", "birkhoff_abi_version",
+    "project", "project_bwd", "sinkhorn", "BirkhoffProjection",
+]
+
+_PKG = pathlib.Path(__file__).resolve().parent
+_LIB_PATH = _PKG / "libbirkhoff.so"
+_lib = None
+
+
+class BirkhoffError(RuntimeError):
+    """A libbirkhoff call returned a non-zero code."""
+
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__("%s: %s (code %d)" % (where, birkhoff_strerror(code), code))
+
+
+def library_path() -> pathlib.Path:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libbirkhoff.so (built in-tree by birkhoff_projection_amd.build); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not _LIB_PATH.exists():
+        raise RuntimeError("libbirkhoff.so is not built (%s); run `python -m birkhoff_projection_amd.build` "
+                           "or __graft_entry__.build()" % _LIB_PATH)
+    lib = ctypes.CDLL(str(_LIB_PATH))
+    vp, i64, ci, cf = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    sig = {
+        "birkhoff_fwd": [vp, vp, vp, i64, ci, cf, ci, vp],
+        "birkhoff_fwd_ex": [vp, vp, vp, vp, i64, ci, cf, ci, vp],
+        "birkhoff_bwd": [vp, vp, vp, vp, i64, ci, vp],
+        "sinkhorn_fwd": [vp, vp, i64, ci, ci, vp],
+        "birkhoff_fwd_bf16": [vp, vp, vp, i64, ci, cf, ci, vp],
+        "birkhoff_bwd_bf16": [vp, vp, vp, vp, i64, ci, vp],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ci
+    lib.birkhoff_strerror.argtypes = [ci]
+    lib.birkhoff_strerror.restype = ctypes.c_char_p
+    lib.birkhoff_abi_version.argtypes = []
+    lib.birkhoff_abi_version.restype = ci
+    _lib = lib
+    return lib
+
+
+def birkhoff_strerror(code: int) -> str:
+    return load_library().birkhoff_strerror(int(code)).decode()
+
+
+def birkhoff_abi_version() -> int:
+    return int(load_library().birkhoff_abi_version())
+
+
+# ---------------------------------------------------------------- marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _mats(x, name, dtype, B=None, n=None):
+    torch = _torch()
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not x.is_cuda:
+        raise ValueError("%s must be on a GPU device" % name)
+    if x.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, x.dtype))
+    if x.dim() != 3 or x.shape[1] != x.shape[2]:
+        raise ValueError("%s must have shape [B, n, n], got %s" % (name, tuple(x.shape)))
+    if not x.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if B is not None and (x.shape[0] != B or x.shape[1] != n):
+        raise ValueError("%s must have shape [%d, %d, %d], got %s" % (name, B, n, n, tuple(x.shape)))
+    return x
+
+
+def _vec(x, name, B, n, dtype):
+    torch = _torch()
+    if not isinstance(x, torch.Tensor) or not x.is_cuda or x.dtype != dtype or not x.is_contiguous():
+        raise ValueError("%s must be a contiguous %s GPU tensor" % (name, dtype))
+    if tuple(x.shape) != ((B, n) if n is not None else (B,)):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(x.shape), (B, n) if n else (B,)))
+    return x
+
+
+def _same_device(*ts):
+    d = ts[0].device
+    for t in ts[1:]:
+        if t.device != d:
+            raise ValueError("all tensors must be on the same device")
+    return d
+
+
+def _call(name, device, *args):
+    torch = _torch()
+    with torch.cuda.device(device):
+        rc = getattr(load_library(), name)(*args)
+    if rc != 0:
+        raise BirkhoffError(rc, name)
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+# ------------------------------------------------------------- ABI wrappers
+
+def birkhoff_fwd(logits, T, dual, tol: float = 1e-6, max_iter: int = 50, stream=None) -> None:
+    """Forward projection into preallocated T [B,n,n] and dual [B,n] (fp32)."""
+    torch = _torch()
+    _mats(logits, "logits", torch.float32)
+    B, n = logits.shape[0], logits.shape[1]
+    _mats(T, "T", torch.float32, B, n)
+    _vec(dual, "dual", B, n, torch.float32)
+    dev = _same_device(logits, T, dual)
+    _call("birkhoff_fwd", dev, _p(logits), _p(T), _p(dual), B, n, float(tol), int(max_iter),
+          _stream_handle(stream, dev))
+
+
+def birkhoff_fwd_ex(logits, T, dual, iters, tol: float = 1e-6, max_iter: int = 50, stream=None) -> None:
+    """As birkhoff_fwd, also writing iters [B] int32 (updates used, -1 if tol not reached)."""
+    torch = _torch()
+    _mats(logits, "logits", torch.float32)
+    B, n = logits.shape[0], logits.shape[1]
+    _mats(T, "T", torch.float32, B, n)
+    _vec(dual, "dual", B, n, torch.float32)
+    _vec(iters, "iters", B, None, torch.int32)
+    dev = _same_device(logits, T, dual, iters)
+    _call("birkhoff_fwd_ex", dev, _p(logits), _p(T), _p(dual), _p(iters), B, n, float(tol), int(max_iter),
+          _stream_handle(stream, dev))
+
+
+def birkhoff_bwd(logits, dual, dT, dH, stream=None) -> None:
+    """Backward: dH = dL/dlogits from dT = dL/dT, at the forward's dual (fp32)."""
+    torch = _torch()
+    _mats(logits, "logits", torch.float32)
+    B, n = logits.shape[0], logits.shape[1]
+    _vec(dual, "dual", B, n, torch.float32)
+    _mats(dT, "dT", torch.float32, B, n)
+    _mats(dH, "dH", torch.float32, B, n)
+    dev = _same_device(logits, dual, dT, dH)
+    _call("birkhoff_bwd", dev, _p(logits), _p(dual), _p(dT), _p(dH), B, n, _stream_handle(stream, dev))
+
+
+def sinkhorn_fwd(logits, T, iters: int = 20, stream=None) -> None:
+    """Baseline: exactly `iters` Sinkhorn-Knopp sweeps (fp32) into preallocated T."""
+    torch = _torch()
+    _mats(logits, "logits", torch.float32)
+    B, n = logits.shape[0], logits.shape[1]
+    _mats(T, "T", torch.float32, B, n)
+    dev = _same_device(logits, T)
+    _call("sinkhorn_fwd", dev, _p(logits), _p(T), B, n, int(iters), _stream_handle(stream, dev))
+
+
+def _bf16_mats(x, name, B=None, n=None):
+    """bf16 storage is passed as torch.bfloat16 (or int16 / uint16 bit patterns)."""
+    torch = _torch()
+    if x.dtype not in (torch.bfloat16, torch.int16, getattr(torch, "uint16", torch.int16)):
+        raise TypeError("%s must be bfloat16 (or 16-bit bf16 bit patterns), got %s" % (name, x.dtype))
+    return _mats(x, name, x.dtype, B, n)
+
+
+def birkhoff_fwd_bf16(logits, T, dual, tol: float = 1e-6, max_iter: int = 50, stream=None) -> None:
+    """Forward with bf16 storage of logits and T (fp32 arithmetic and fp32 dual)."""
+    torch = _torch()
+    _bf16_mats(logits, "logits")
+    B, n = logits.shape[0], logits.shape[1]
+    _bf16_mats(T, "T", B, n)
+    _vec(dual, "dual", B, n, torch.float32)
+    dev = _same_device(logits, T, dual)
+    _call("birkhoff_fwd_bf16", dev, _p(logits), _p(T), _p(dual), B, n, float(tol), int(max_iter),
+          _stream_handle(stream, dev))
+
+
+def birkhoff_bwd_bf16(logits, dual, dT, dH, stream=None) -> None:
+    """Backward with bf16 storage of logits, dT and dH (fp32 arithmetic and fp32 dual)."""
+    torch = _torch()
+    _bf16_mats(logits, "logits")
+    B, n = logits.shape[0], logits.shape[1]
+    _vec(dual, "dual", B, n, torch.float32)
+    _bf16_mats(dT, "dT", B, n)
+    _bf16_mats(dH, "dH", B, n)
+    dev = _same_device(logits, dual, dT, dH)
+    _call("birkhoff_bwd_bf16", dev, _p(logits), _p(dual), _p(dT), _p(dH), B, n, _stream_handle(stream, dev))
+
+
+# ------------------------------------------------------- allocating helpers
+
+def project(logits, tol: float = 1e-6, max_iter: int = 50, stream=None):
+    """Allocate outputs and run the forward pass. Returns (T, dual); bf16 input gives bf16 T."""
+    torch = _torch()
+    B, n = logits.shape[0], logits.shape[1]
+    dual = torch.empty((B, n), dtype=torch.float32, device=logits.device)
+    T = torch.empty_like(logits, memory_format=torch.contiguous_format)
+    if logits.dtype == torch.float32:
+        birkhoff_fwd(logits, T, dual, tol, max_iter, stream)
+    else:
+        birkhoff_fwd_bf16(logits, T, dual, tol, max_iter, stream)
+    return T, dual
+
+
+def project_bwd(logits, dual, dT, stream=None):
+    """Allocate dH and run the backward pass."""
+    torch = _torch()
+    dH = torch.empty_like(dT, memory_format=torch.contiguous_format)
+    if logits.dtype == torch.float32:
+        birkhoff_bwd(logits, dual, dT, dH, stream)
+    else:
+        birkhoff_bwd_bf16(logits, dual, dT, dH, stream)
+    return dH
+
+
+def sinkhorn(logits, iters: int = 20, stream=None):
+    T = _torch().empty_like(logits, memory_format=_torch().contiguous_format)
+    sinkhorn_fwd(logits, T, iters, stream)
+    return T
+
+
+def _autograd_function():
+    torch = _torch()
+
+    class BirkhoffProjection(torch.autograd.Function):
+        """T = proj_KL(exp(logits)) onto B_n with the implicit (eq 13) backward.
+
+        Saves only (logits, dual); no Newton iterates are kept.
+        """
+
+        @staticmethod
+        def forward(ctx, logits, tol: float = 1e-6, max_iter: int = 50):
+            logits = logits.contiguous()
+            T, dual = project(logits, tol, max_iter)
+            ctx.save_for_backward(logits, dual)
+            return T
+
+        @staticmethod
+        def backward(ctx, dT):
+            logits, dual = ctx.saved_tensors
+            return project_bwd(logits, dual, dT.contiguous()), None, None
+
+    return BirkhoffProjection
+
+
+class _LazyFunction:
+    _fn = None
+
+    def __getattr__(self, item):
+        if _LazyFunction._fn is None:
+            _LazyFunction._fn = _autograd_function()
+        return getattr(_LazyFunction._fn, item)
+
+
+BirkhoffProjection = _LazyFunction()

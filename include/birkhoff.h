@@ -1,0 +1,112 @@
+/*
+ * birkhoff.h -- C ABI of libbirkhoff, batched KL projection onto the Birkhoff
+ * polytope for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  For every one of B independent n x n logit matrices H
+ * (n = 4 or n = 8) the forward pass returns
+ *
+ *     T = argmin_{P in B_n} KL(P || exp(H)),      B_n = doubly stochastic n x n,
+ *
+ * i.e. the unique T = D1 exp(H) D2 with unit row and column sums
+ * ("Accelerating Birkhoff Projection for Manifold-Constrained Hyper-Connections",
+ * section 2.2, eq (1); Sinkhorn's theorem).  It is found by Newton's method on
+ * the reduced (n-1)-dimensional entropic-OT dual (section 3.1, eqs (8)-(9);
+ * section 3.2, eqs (10)-(12) for n = 4) with the step-size rule and Sinkhorn
+ * fallback of the author's blog post "小矩阵遇上牛顿法" (section 2.2).  The
+ * backward pass returns dL/dH from dL/dT by implicit differentiation at the
+ * optimal dual (section 4.1, eq (13); section 4.2), without unrolling.
+ *
+ * Conventions shared by every entry point.
+ *   - All array pointers are DEVICE pointers owned by the caller (for example
+ *     torch tensors on the GPU).  The library never allocates, frees or keeps
+ *     them, and holds no global mutable state; calls are thread-safe.
+ *   - Matrices are contiguous, row-major and stored back to back: element
+ *     (b, i, j) of an [B, n, n] array is at offset (b*n + i)*n + j.
+ *     The dual is [B, n] fp32: dual[b*n + j] = beta_j of matrix b, with the
+ *     gauge beta_{n-1} = 0 (zero-based last column) stored explicitly.
+ *   - Every pointer must be 16-byte aligned (iters of birkhoff_fwd_ex: 4-byte
+ *     aligned); arrays must not overlap.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *     Work is enqueued asynchronously on it; nothing synchronizes.
+ *   - B == 0 is a no-op that returns BIRKHOFF_OK (pointers may then be NULL).
+ *   - Arguments are validated on the host before any HIP call; a rejected
+ *     call enqueues nothing.
+ *   - A matrix that does not reach `tol` within `max_iter` updates is not an
+ *     error: its last iterate is written (see birkhoff_fwd_ex to detect it).
+ *     Non-finite logits yield NaN in that matrix's outputs only.
+ *
+ * Return codes: BIRKHOFF_OK or one of the negative BIRKHOFF_E* codes below;
+ * birkhoff_strerror() describes them.
+ */
+#ifndef BIRKHOFF_H
+#define BIRKHOFF_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BIRKHOFF_OK 0
+#define BIRKHOFF_EINVAL (-1)  /* NULL pointer with B > 0, B < 0, unsupported n, tol <= 0 or NaN,
+                                 max_iter < 1, iters < 1, or B too large for one launch */
+#define BIRKHOFF_EALIGN (-2)  /* a pointer is not 16-byte aligned (iters: not 4-byte aligned) */
+#define BIRKHOFF_ELAUNCH (-3) /* the HIP runtime reported an error at launch (hipGetLastError) */
+
+/* Forward pass, fp32 storage.
+ *   logits   [B, n, n] fp32, input H
+ *   T        [B, n, n] fp32, output: the projection of exp(H) onto B_n
+ *   dual     [B, n]    fp32, output: beta with beta_{n-1} = 0, such that
+ *            T_ij = exp(H_ij + beta_j) / sum_k exp(H_ik + beta_k)
+ *            (section 3.1: rows of T are Softmax(H_i. + beta)); it is the only
+ *            state the backward pass needs
+ *   n        4 or 8
+ *   tol      stop when every column sum of T is within tol of 1 (rows sum to one
+ *            by construction); typical 1e-6
+ *   max_iter cap on Newton updates (an accepted step or a fallback sweep), >= 1
+ */
+int birkhoff_fwd(const float* logits, float* T, float* dual, int64_t B, int n,
+                 float tol, int max_iter, void* stream);
+
+/* As birkhoff_fwd, and additionally writes iters[b] (int32, [B]): the number of
+ * updates matrix b took to reach tol, or -1 when it did not reach tol within
+ * max_iter updates (or its input was not finite).  iters must be non-NULL. */
+int birkhoff_fwd_ex(const float* logits, float* T, float* dual, int32_t* iters,
+                    int64_t B, int n, float tol, int max_iter, void* stream);
+
+/* Backward pass, fp32 storage (section 4.1 eq (13), section 4.2).
+ *   logits [B, n, n] fp32, the forward input H
+ *   dual   [B, n]    fp32, the forward's dual output
+ *   dT     [B, n, n] fp32, upstream gradient dL/dT
+ *   dH     [B, n, n] fp32, output dL/dH (sign already flipped from dL/dM, H = -M)
+ * T is recomputed from (logits, dual); the Newton iterates are not needed. */
+int birkhoff_bwd(const float* logits, const float* dual, const float* dT, float* dH,
+                 int64_t B, int n, void* stream);
+
+/* Comparison baseline: exactly `iters` Sinkhorn-Knopp sweeps (section 2.2 eq (2),
+ * evaluated in the log domain as the block coordinate ascent of eq (7)) from
+ * v = 1, then T = diag(u) exp(H) diag(v).  One sweep = row then column
+ * normalisation, so after it the columns sum to one and the rows carry the error.
+ *   logits [B, n, n] fp32 input, T [B, n, n] fp32 output, iters >= 1. */
+int sinkhorn_fwd(const float* logits, float* T, int64_t B, int n, int iters, void* stream);
+
+/* bf16-storage variants: logits, T, dT and dH hold bfloat16 bit patterns
+ * (uint16_t), the dual stays fp32; all arithmetic is fp32 and T / dH are
+ * rounded to bf16 (nearest, ties to even) when stored.  Otherwise identical to
+ * the fp32 entry points. */
+int birkhoff_fwd_bf16(const uint16_t* logits, uint16_t* T, float* dual, int64_t B, int n,
+                      float tol, int max_iter, void* stream);
+int birkhoff_bwd_bf16(const uint16_t* logits, const float* dual, const uint16_t* dT,
+                      uint16_t* dH, int64_t B, int n, void* stream);
+
+/* Static description of a return code (never NULL). */
+const char* birkhoff_strerror(int code);
+
+/* ABI version, currently 1. */
+int birkhoff_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BIRKHOFF_H */

@@ -1,0 +1,113 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import math
+import pathlib
+import re
+
+import pytest
+
+import birkhoff_projection_amd as bp
+
+ROOT = pathlib.Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "birkhoff.h"
+
+EINVAL, EALIGN = -1, -2
+
+
+def declared_symbols():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not bp.library_path().exists():
+        from birkhoff_projection_amd import build
+        build.build()
+    return bp.load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_symbols()
+    for n in ("birkhoff_fwd", "birkhoff_fwd_ex", "birkhoff_bwd", "sinkhorn_fwd",
+              "birkhoff_fwd_bf16", "birkhoff_bwd_bf16", "birkhoff_strerror", "birkhoff_abi_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strerror(lib):
+    assert bp.birkhoff_abi_version() == 1
+    for code in (0, -1, -2, -3, 12345):
+        s = bp.birkhoff_strerror(code)
+        assert isinstance(s, str) and s
+
+
+A = 1 << 20          # fake, 16-byte aligned addresses: never dereferenced on a rejected call
+P = [A, A + 4096, A + 8192, A + 12288]
+
+
+def fwd(lib, *a):
+    return lib.birkhoff_fwd(*a)
+
+
+@pytest.mark.parametrize("B,n,tol,it,want", [
+    (-1, 4, 1e-6, 50, EINVAL),
+    (5, 3, 1e-6, 50, EINVAL),
+    (5, 16, 1e-6, 50, EINVAL),
+    (5, 4, 0.0, 50, EINVAL),
+    (5, 4, -1.0, 50, EINVAL),
+    (5, 4, math.nan, 50, EINVAL),
+    (5, 4, math.inf, 50, EINVAL),
+    (5, 4, 1e-6, 0, EINVAL),
+    (1 << 50, 4, 1e-6, 50, EINVAL),
+    (0, 4, 1e-6, 50, 0),
+])
+def test_forward_argument_checks(lib, B, n, tol, it, want):
+    assert lib.birkhoff_fwd(P[0], P[1], P[2], B, n, tol, it, None) == want
+    assert lib.birkhoff_fwd_bf16(P[0], P[1], P[2], B, n, tol, it, None) == want
+    assert lib.birkhoff_fwd_ex(P[0], P[1], P[2], P[3], B, n, tol, it, None) == want
+
+
+def test_null_and_misaligned_pointers(lib):
+    B, n = 7, 4
+    for k in range(3):
+        ptrs = list(P[:3])
+        ptrs[k] = None
+        assert lib.birkhoff_fwd(*ptrs, B, n, 1e-6, 50, None) == EINVAL
+        ptrs[k] = P[k] + 4
+        assert lib.birkhoff_fwd(*ptrs, B, n, 1e-6, 50, None) == EALIGN
+    assert lib.birkhoff_fwd_ex(P[0], P[1], P[2], None, B, n, 1e-6, 50, None) == EINVAL
+    assert lib.birkhoff_fwd_ex(P[0], P[1], P[2], P[3] + 2, B, n, 1e-6, 50, None) == EALIGN
+    for k in range(4):
+        ptrs = list(P)
+        ptrs[k] = None
+        assert lib.birkhoff_bwd(*ptrs, B, n, None) == EINVAL
+        assert lib.birkhoff_bwd_bf16(*ptrs, B, n, None) == EINVAL
+        ptrs[k] = P[k] + 2
+        assert lib.birkhoff_bwd(*ptrs, B, n, None) == EALIGN
+    assert lib.sinkhorn_fwd(None, P[1], B, n, 20, None) == EINVAL
+    assert lib.sinkhorn_fwd(P[0] + 4, P[1], B, n, 20, None) == EALIGN
+
+
+def test_backward_and_sinkhorn_argument_checks(lib):
+    assert lib.birkhoff_bwd(*P, -1, 4, None) == EINVAL
+    assert lib.birkhoff_bwd(*P, 5, 5, None) == EINVAL
+    assert lib.birkhoff_bwd(None, None, None, None, 0, 8, None) == 0
+    assert lib.sinkhorn_fwd(P[0], P[1], 5, 4, 0, None) == EINVAL
+    assert lib.sinkhorn_fwd(P[0], P[1], 5, 4, -3, None) == EINVAL
+    assert lib.sinkhorn_fwd(P[0], P[1], 5, 7, 20, None) == EINVAL
+    assert lib.sinkhorn_fwd(None, None, 0, 4, 20, None) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import birkhoff_projection_amd as mod
+    monkeypatch.setattr(mod, "_lib", None)
+    monkeypatch.setattr(mod, "_LIB_PATH", tmp_path / "missing.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        mod.load_library()

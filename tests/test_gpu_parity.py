@@ -1,0 +1,366 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on the
+same seeded inputs.  Needs an MI355X; run with -m gpu.
+
+Gates (fp32 storage):
+  forward   max |T - T_ref| <= 1e-5 over every entry;
+  residual  max(|rowsum - 1|, |colsum - 1|) of the GPU's T, summed in float64, <= 1e-5;
+  backward  per matrix max|dH - dH_ref| / max|dH_ref| <= 1e-4.
+bf16 storage adds half a bf16 ulp of the reference value to the T and dH gates
+(an fp32-exact answer must still be rounded once to be stored), and takes the
+residual on T rebuilt in float64 from the logits and the fp32 dual.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from birkhoff_projection_amd import workloads as W
+
+torch = pytest.importorskip("torch")
+import birkhoff_projection_amd as bp  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+FWD_TOL = 1e-5
+RES_TOL = 1e-5
+BWD_TOL = 1e-4
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def as_storage(a, w):
+    """numpy storage array -> device tensor of the ABI's storage dtype."""
+    t = dev(a)
+    return t.view(torch.bfloat16) if w.io == "bf16" else t
+
+
+def host_f64(t):
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy().astype(np.float64)
+    return t.cpu().numpy().astype(np.float64)
+
+
+def half_ulp_bf16(x):
+    """Half a bf16 ulp of |x| (bf16 has 8 significant bits)."""
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    return np.where(ax > 0, 2.0 ** (e - 8), 0.0)
+
+
+def residual(T):
+    return np.maximum(np.abs(T.sum(axis=-1) - 1).max(axis=-1), np.abs(T.sum(axis=-2) - 1).max(axis=-1))
+
+
+def rebuilt_T(H, dual):
+    """Row softmax of H + beta in float64 (the dual's own projection)."""
+    U = H + dual[:, None, :]
+    U = U - U.max(axis=2, keepdims=True)
+    E = np.exp(U)
+    return E / E.sum(axis=2, keepdims=True)
+
+
+def run_fwd(w, Hs, stats=False):
+    B, n = Hs.shape[0], w.n
+    H = as_storage(Hs, w)
+    T = torch.empty_like(H)
+    dual = torch.empty((B, n), dtype=torch.float32, device=DEV)
+    iters = None
+    if w.io == "bf16":
+        bp.birkhoff_fwd_bf16(H, T, dual, w.tol, w.max_iter)
+    elif stats:
+        iters = torch.empty(B, dtype=torch.int32, device=DEV)
+        bp.birkhoff_fwd_ex(H, T, dual, iters, w.tol, w.max_iter)
+    else:
+        bp.birkhoff_fwd(H, T, dual, w.tol, w.max_iter)
+    return H, T, dual, iters
+
+
+def run_bwd(w, H, dual, Gs):
+    G = as_storage(Gs, w)
+    dH = torch.empty_like(G)
+    if w.io == "bf16":
+        bp.birkhoff_bwd_bf16(H, dual, G, dH)
+    else:
+        bp.birkhoff_bwd(H, dual, G, dH)
+    return dH
+
+
+def check_forward(w, H64, T_gpu, dual_gpu, T_ref):
+    err = np.abs(T_gpu - T_ref)
+    if w.io == "bf16":
+        assert (err <= FWD_TOL + half_ulp_bf16(T_ref)).all(), err.max()
+        res = residual(rebuilt_T(H64, dual_gpu)).max()
+    else:
+        assert err.max() <= FWD_TOL, err.max()
+        res = residual(T_gpu).max()
+    assert res <= RES_TOL, res
+    return err.max(), res
+
+
+def check_backward(w, dH_gpu, dH_ref):
+    scale = np.abs(dH_ref).max(axis=(1, 2))
+    diff = np.abs(dH_gpu - dH_ref)
+    if w.io == "bf16":
+        ok = diff <= BWD_TOL * scale[:, None, None] + half_ulp_bf16(dH_ref)
+        assert ok.all(), diff.max()
+        return float((diff.max(axis=(1, 2)) / np.where(scale > 0, scale, 1.0)).max())
+    rel = diff.max(axis=(1, 2)) / np.where(scale > 1e-30, scale, 1.0)
+    assert rel.max() <= BWD_TOL, rel.max()
+    return float(rel.max())
+
+
+# ----------------------------------------------------- whole-batch parity
+
+@pytest.mark.parametrize("key,B", [("pr1", None), ("train", 8192 + 37), ("n8", 4096 + 19),
+                                   ("hard", 8192 + 37), ("bw", 8192 + 37)])
+def test_parity_whole_batch(key, B):
+    w = W.WORKLOADS[key]
+    print("case", key, B, flush=True)
+    Hs = W.make_logits(w, B=B)
+    H64 = W.decode_f64(Hs)
+    H, T, dual, _ = run_fwd(w, Hs)
+    T_ref, beta_ref, st = oracle.project(H64, sk_cap=w.sk_cap)
+    assert (st >= 0).all()
+    T_gpu = host_f64(T)
+    dual_gpu = dual.cpu().numpy().astype(np.float64)
+    err, res = check_forward(w, H64, T_gpu, dual_gpu, T_ref)
+    assert (dual_gpu[:, -1] == 0).all()
+    if key in ("pr1", "train"):   # well-conditioned duals are determined to fp32 accuracy
+        assert np.abs(dual_gpu - beta_ref).max() <= 1e-4
+    if w.upstream is not None:
+        Gs = W.make_upstream(w, B=B)
+        dH = run_bwd(w, H, dual, Gs)
+        dH_ref = oracle.bwd(T_ref, W.decode_f64(Gs))
+        rel = check_backward(w, host_f64(dH), dH_ref)
+        print("  fwd err %.2e res %.2e bwd rel %.2e" % (err, res, rel))
+
+
+# ---------------------------------------------- full sizes, sampled outputs
+
+def sample_indices(B, k=2048, seed=0):
+    rng = np.random.default_rng(seed)
+    idx = np.concatenate([np.arange(min(64, B)), np.arange(max(0, B - 64), B), rng.integers(0, B, k)])
+    return np.unique(idx)
+
+
+@pytest.mark.parametrize("key", ["train", "hard", "n8", "bw"])
+def test_parity_full_size_sampled(key):
+    """Full batch in the benchmark's launch configuration; the oracle checks a
+    sample of matrices one by one and the residual is checked on every output."""
+    w = W.WORKLOADS[key]
+    print("case full", key, w.B, flush=True)
+    Hs = W.make_logits(w)
+    H, T, dual, _ = run_fwd(w, Hs)
+    Gs = W.make_upstream(w) if w.upstream is not None else None
+    dH = run_bwd(w, H, dual, Gs) if Gs is not None else None
+    torch.cuda.synchronize()
+    # residual of every output, in float64 on the device (a property at any size)
+    if w.io == "bf16":
+        Hd = H.double()
+        U = Hd + dual.double()[:, None, :]
+        Tr = torch.softmax(U, dim=2)
+        res = torch.maximum((Tr.sum(2) - 1).abs().amax(1), (Tr.sum(1) - 1).abs().amax(1)).max().item()
+        del Hd, U, Tr
+    else:
+        Td = T.double()
+        res = torch.maximum((Td.sum(2) - 1).abs().amax(1), (Td.sum(1) - 1).abs().amax(1)).max().item()
+        del Td
+    assert res <= RES_TOL, res
+    assert torch.isfinite(T.float()).all().item()
+    idx = sample_indices(w.B)
+    it = torch.from_numpy(idx).to(DEV)
+    H64 = W.decode_f64(Hs[idx])
+    T_ref, _, st = oracle.project(H64, sk_cap=w.sk_cap)
+    assert (st >= 0).all()
+    T_s = host_f64(T[it])
+    d_s = dual[it].cpu().numpy().astype(np.float64)
+    check_forward(w, H64, T_s, d_s, T_ref)
+    if dH is not None:
+        dH_ref = oracle.bwd(T_ref, W.decode_f64(Gs[idx]))
+        check_backward(w, host_f64(dH[it]), dH_ref)
+
+
+# ------------------------------------------------------------ edge cases
+
+@pytest.mark.parametrize("B", [1, 2, 63, 64, 65, 255, 256, 257, 1000])
+@pytest.mark.parametrize("n", [4, 8])
+def test_ragged_batches_and_canaries(B, n):
+    """Outputs land exactly in their slots: padding before and after each output
+    buffer keeps its sentinel; results match the oracle."""
+    print("case ragged", B, n, flush=True)
+    w = W.WORKLOADS["pr1" if n == 4 else "n8"]
+    Hs = W.make_logits(w, B=B, seed=1000 + B)
+    Gs = W.make_upstream(w, B=B, seed=2000 + B)
+    pad = 3
+    sentinel = 12345.0
+    H = dev(Hs)
+    G = dev(Gs)
+    Tbuf = torch.full((B + 2 * pad, n, n), sentinel, device=DEV)
+    Dbuf = torch.full((B + 2 * pad, n), sentinel, device=DEV)
+    Hbuf = torch.full((B + 2 * pad, n, n), sentinel, device=DEV)
+    Sbuf = torch.full((B + 2 * pad, n, n), sentinel, device=DEV)
+    Ibuf = torch.full((B + 2 * pad,), -7, dtype=torch.int32, device=DEV)
+    T, dual, dH, S, it = Tbuf[pad:pad + B], Dbuf[pad:pad + B], Hbuf[pad:pad + B], Sbuf[pad:pad + B], Ibuf[pad:pad + B]
+    bp.birkhoff_fwd_ex(H, T, dual, it, w.tol, w.max_iter)
+    bp.birkhoff_bwd(H, dual, G, dH)
+    bp.sinkhorn_fwd(H, S, 20)
+    torch.cuda.synchronize()
+    for buf in (Tbuf, Dbuf, Hbuf, Sbuf):
+        assert (buf[:pad] == sentinel).all() and (buf[pad + B:] == sentinel).all()
+    assert (Ibuf[:pad] == -7).all() and (Ibuf[pad + B:] == -7).all()
+    T_ref, _, _ = oracle.project(Hs.astype(np.float64))
+    check_forward(w, Hs.astype(np.float64), host_f64(T), dual.cpu().numpy().astype(np.float64), T_ref)
+    check_backward(w, host_f64(dH), oracle.bwd(T_ref, Gs.astype(np.float64)))
+    assert (it.cpu().numpy() >= 0).all()
+    np.testing.assert_allclose(host_f64(S), oracle.sinkhorn_k(Hs.astype(np.float64), 20), rtol=0, atol=1e-5)
+
+
+def test_bf16_ragged_canaries():
+    w = W.WORKLOADS["bw"]
+    B, pad = 77, 8   # pad of 8 bf16 matrices keeps 16-byte alignment
+    Hs = W.make_logits(w, B=B, seed=31)
+    Gs = W.make_upstream(w, B=B, seed=32)
+    H = as_storage(Hs, w)
+    G = as_storage(Gs, w)
+    Tbuf = torch.full((B + 2 * pad, 4, 4), 3.0, device=DEV, dtype=torch.bfloat16)
+    Hbuf = torch.full((B + 2 * pad, 4, 4), 3.0, device=DEV, dtype=torch.bfloat16)
+    dual = torch.empty((B, 4), device=DEV)
+    T, dH = Tbuf[pad:pad + B], Hbuf[pad:pad + B]
+    bp.birkhoff_fwd_bf16(H, T, dual, w.tol, w.max_iter)
+    bp.birkhoff_bwd_bf16(H, dual, G, dH)
+    torch.cuda.synchronize()
+    for buf in (Tbuf, Hbuf):
+        assert (buf[:pad] == 3.0).all() and (buf[pad + B:] == 3.0).all()
+    H64 = W.decode_f64(Hs)
+    T_ref, _, _ = oracle.project(H64)
+    check_forward(w, H64, host_f64(T), dual.cpu().numpy().astype(np.float64), T_ref)
+    check_backward(w, host_f64(dH), oracle.bwd(T_ref, W.decode_f64(Gs)))
+
+
+def test_empty_batch_is_a_noop():
+    H = torch.empty((0, 4, 4), device=DEV)
+    T, dual = bp.project(H)
+    assert T.shape == (0, 4, 4) and dual.shape == (0, 4)
+    assert bp.project_bwd(H, dual, torch.empty((0, 4, 4), device=DEV)).shape == (0, 4, 4)
+    assert bp.sinkhorn(H).shape == (0, 4, 4)
+
+
+@pytest.mark.parametrize("n", [4, 8])
+def test_special_inputs(n):
+    """Exactly known projections: doubly stochastic inputs with row/column shifts
+    map to themselves, rank-one inputs map to J/n, constant inputs to J/n."""
+    rng = np.random.default_rng(5)
+    B = 300
+    P = np.empty((B, n, n))
+    for b in range(B):
+        wts = rng.dirichlet(np.ones(5))
+        M = np.zeros((n, n))
+        for k in range(5):
+            M[np.arange(n), rng.permutation(n)] += wts[k]
+        P[b] = 0.9 * M + 0.1 / n
+    a, c = rng.standard_normal((B, n, 1)), rng.standard_normal((B, 1, n))
+    H = (np.log(P) + a + c).astype(np.float32)
+    T, dual = bp.project(dev(H))
+    np.testing.assert_allclose(host_f64(T), P, rtol=0, atol=2e-5)
+    R = (a + c + np.zeros((1, n, n))).astype(np.float32)
+    T1, _ = bp.project(dev(R))
+    np.testing.assert_allclose(host_f64(T1), 1.0 / n, rtol=0, atol=1e-6)
+    T0, d0 = bp.project(torch.zeros((5, n, n), device=DEV))
+    assert (host_f64(T0) == 1.0 / n).all() and (d0.cpu().numpy() == 0).all()
+
+
+def test_nonfinite_inputs_stay_in_their_matrix():
+    w = W.WORKLOADS["pr1"]
+    Hs = W.make_logits(w, B=300)
+    bad = Hs.copy()
+    bad[5, 1, 2] = np.nan
+    bad[9, 0, 0] = np.inf
+    bad[200, 3, 3] = -np.inf
+    T0, d0 = bp.project(dev(Hs))
+    T1, d1 = bp.project(dev(bad))
+    torch.cuda.synchronize()
+    t0, t1 = T0.cpu().numpy(), T1.cpu().numpy()
+    keep = np.setdiff1d(np.arange(300), [5, 9, 200])
+    assert np.array_equal(t0[keep], t1[keep])
+    assert np.isnan(t1[5]).any() and np.isnan(t1[9]).any()
+    iters = torch.empty(300, dtype=torch.int32, device=DEV)
+    T2 = torch.empty_like(T1)
+    d2 = torch.empty_like(d1)
+    bp.birkhoff_fwd_ex(dev(bad), T2, d2, iters)
+    assert iters[5].item() == -1 and iters[9].item() == -1
+
+
+def test_max_iter_one_and_stats():
+    w = W.WORKLOADS["hard"]
+    Hs = W.make_logits(w, B=4096)
+    H = dev(Hs)
+    T = torch.empty_like(H)
+    dual = torch.empty((4096, 4), device=DEV)
+    it = torch.empty(4096, dtype=torch.int32, device=DEV)
+    bp.birkhoff_fwd_ex(H, T, dual, it, 1e-6, 1)
+    assert torch.isfinite(T).all().item()
+    assert ((it == -1) | (it <= 1)).all().item()
+    bp.birkhoff_fwd_ex(H, T, dual, it, w.tol, w.max_iter)
+    itn = it.cpu().numpy()
+    assert (itn >= 0).all(), (itn < 0).sum()        # every hard matrix converges within 100 updates
+    T2 = torch.empty_like(T)
+    bp.birkhoff_fwd(H, T2, torch.empty_like(dual), w.tol, w.max_iter)
+    assert torch.equal(T, T2)                        # the stats variant computes the same thing
+    print("iterations: mean %.2f max %d" % (itn.mean(), itn.max()))
+
+
+def test_repeatable_and_stream_ordered():
+    w = W.WORKLOADS["train"]
+    Hs = W.make_logits(w, B=50_000)
+    Gs = W.make_upstream(w, B=50_000)
+    H, G = dev(Hs), dev(Gs)
+    T1, d1 = bp.project(H)
+    dH1 = bp.project_bwd(H, d1, G)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        T2, d2 = bp.project(H)
+        dH2 = bp.project_bwd(H, d2, G)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert torch.equal(T1, T2) and torch.equal(d1, d2) and torch.equal(dH1, dH2)
+
+
+def test_autograd_function_matches_oracle():
+    w = W.WORKLOADS["pr1"]
+    Hs = W.make_logits(w, B=512)
+    Gs = W.make_upstream(w, B=512)
+    H = dev(Hs).requires_grad_(True)
+    T = bp.BirkhoffProjection.apply(H)
+    (T * dev(Gs)).sum().backward()
+    T_ref, _, _ = oracle.project(Hs.astype(np.float64))
+    assert np.abs(host_f64(T.detach()) - T_ref).max() <= FWD_TOL
+    check_backward(w, host_f64(H.grad), oracle.bwd(T_ref, Gs.astype(np.float64)))
+
+
+@pytest.mark.parametrize("K", [1, 5, 20])
+@pytest.mark.parametrize("key", ["pr1", "hard", "n8"])
+def test_sinkhorn_baseline_matches_oracle(key, K):
+    w = W.WORKLOADS[key]
+    Hs = W.make_logits(w, B=4096 + 13)
+    T = bp.sinkhorn(dev(Hs), K)
+    ref = oracle.sinkhorn_k(Hs.astype(np.float64), K)
+    np.testing.assert_allclose(host_f64(T), ref, rtol=0, atol=1e-5)
+
+
+def test_newton_versus_sinkhorn20_on_hard_inputs():
+    """The pages' qualitative claim (section 5): at large magnitudes 20 Sinkhorn sweeps
+    leave large marginal errors, while Newton's stay small (L1 of row and column sums)."""
+    w = W.WORKLOADS["hard"]
+    Hs = W.make_logits(w, B=65536)
+    H = dev(Hs)
+    T, _ = bp.project(H, w.tol, w.max_iter)
+    S = bp.sinkhorn(H, 20)
+    l1 = lambda X: ((X.double().sum(2) - 1).abs().sum(1) + (X.double().sum(1) - 1).abs().sum(1))
+    e_newton, e_sk = l1(T), l1(S)
+    print("L1 marginal error: newton max %.2e median %.2e | SK-20 max %.2e median %.2e" % (
+        e_newton.max().item(), e_newton.median().item(), e_sk.max().item(), e_sk.median().item()))
+    assert e_newton.max().item() < 1e-4
+    assert e_sk.max().item() > 100 * e_newton.max().item()
