@@ -21,31 +21,29 @@ __device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x);
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float rsq(float x) { return __builtin_amdgcn_rsqf(x); }
 
-// e^x - 1 with relative accuracy for small |x|: degree-8 Taylor polynomial on
-// |x| < 1/2 (truncation below 2e-8 relative), e^x - 1 elsewhere (no cancellation
-// there: |e^x - 1| > 0.39).  `ex` must be e^x.
+// e^x - 1 with relative accuracy for small |x|: degree-6 Taylor polynomial on
+// |x| < 1/16 (truncation below 3e-10 relative), e^x - 1 elsewhere (there the
+// relative rounding error stays below 1.2e-6, and it only enters through
+// quantities that are not close to cancelling).  `ex` must be e^x.
 __device__ __forceinline__ float expm1_from(float x, float ex) {
-    float p = fmaf(x, 1.0f / 40320.0f, 1.0f / 5040.0f);
-    p = fmaf(x, p, 1.0f / 720.0f);
-    p = fmaf(x, p, 1.0f / 120.0f);
+    float p = fmaf(x, 1.0f / 720.0f, 1.0f / 120.0f);
     p = fmaf(x, p, 1.0f / 24.0f);
     p = fmaf(x, p, 1.0f / 6.0f);
     p = fmaf(x, p, 0.5f);
-    float small = fmaf(x * x, p, x);
-    return fabsf(x) < 0.5f ? small : ex - 1.0f;
+    const float small = fmaf(x * x, p, x);
+    return fabsf(x) < 0.0625f ? small : ex - 1.0f;
 }
 
-// log(1 + s) with relative accuracy for small |s|: Taylor series on |s| < 1/16
-// (truncation below 1e-9 relative), log2(1 + s) * ln 2 elsewhere.
-__device__ __forceinline__ float log1p_acc(float s) {
+// log(1 + s) for |s| < 1/16 by its Taylor series to degree 8 (truncation below
+// 1e-9 relative); keeps full relative accuracy as s -> 0.
+__device__ __forceinline__ float log1p_series(float s) {
     float p = fmaf(s, -1.0f / 8.0f, 1.0f / 7.0f);
     p = fmaf(s, p, -1.0f / 6.0f);
     p = fmaf(s, p, 1.0f / 5.0f);
     p = fmaf(s, p, -1.0f / 4.0f);
     p = fmaf(s, p, 1.0f / 3.0f);
     p = fmaf(s, p, -0.5f);
-    float small = fmaf(s * s, p, s);
-    return fabsf(s) < 0.0625f ? small : lg2(1.0f + s) * kLn2;
+    return fmaf(s * s, p, s);
 }
 
 // ---- storage types -------------------------------------------------------
@@ -60,59 +58,181 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float x) {
     return (x != x) ? 0x7FC0u : r;
 }
 
-// Load / store K consecutive elements of a lane's own matrix (K a multiple of 8),
-// as 16-byte vector accesses.
+// Decode / encode one matrix between its storage chunks (16-byte words, as
+// loaded from memory) and fp32 registers.  K elements, K * sizeof(IO) a
+// multiple of 16.
 template <typename IO>
 struct Storage;
 
 template <>
 struct Storage<float> {
     template <int K>
-    __device__ __forceinline__ static void load(const float* __restrict__ p, float (&v)[K]) {
-        const float4* q = reinterpret_cast<const float4*>(p);
+    __device__ __forceinline__ static void decode(const uint4 (&w)[K / 4], float (&v)[K]) {
 #pragma unroll
         for (int k = 0; k < K / 4; ++k) {
-            float4 t = q[k];
-            v[4 * k + 0] = t.x;
-            v[4 * k + 1] = t.y;
-            v[4 * k + 2] = t.z;
-            v[4 * k + 3] = t.w;
+            v[4 * k + 0] = __uint_as_float(w[k].x);
+            v[4 * k + 1] = __uint_as_float(w[k].y);
+            v[4 * k + 2] = __uint_as_float(w[k].z);
+            v[4 * k + 3] = __uint_as_float(w[k].w);
         }
     }
     template <int K>
-    __device__ __forceinline__ static void store(float* __restrict__ p, const float (&v)[K]) {
-        float4* q = reinterpret_cast<float4*>(p);
+    __device__ __forceinline__ static void encode(const float (&v)[K], uint4 (&w)[K / 4]) {
 #pragma unroll
-        for (int k = 0; k < K / 4; ++k) q[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+        for (int k = 0; k < K / 4; ++k)
+            w[k] = make_uint4(__float_as_uint(v[4 * k]), __float_as_uint(v[4 * k + 1]),
+                              __float_as_uint(v[4 * k + 2]), __float_as_uint(v[4 * k + 3]));
     }
 };
 
 template <>
 struct Storage<uint16_t> {
     template <int K>
-    __device__ __forceinline__ static void load(const uint16_t* __restrict__ p, float (&v)[K]) {
-        const uint4* q = reinterpret_cast<const uint4*>(p);
+    __device__ __forceinline__ static void decode(const uint4 (&w)[K / 8], float (&v)[K]) {
 #pragma unroll
         for (int k = 0; k < K / 8; ++k) {
-            uint4 t = q[k];
-            uint32_t w[4] = {t.x, t.y, t.z, t.w};
+            const uint32_t u[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
-                v[8 * k + 2 * h + 0] = bf16_to_f32(w[h] & 0xFFFFu);
-                v[8 * k + 2 * h + 1] = bf16_to_f32(w[h] >> 16);
+                v[8 * k + 2 * h + 0] = bf16_to_f32(u[h] & 0xFFFFu);
+                v[8 * k + 2 * h + 1] = bf16_to_f32(u[h] >> 16);
             }
         }
     }
     template <int K>
-    __device__ __forceinline__ static void store(uint16_t* __restrict__ p, const float (&v)[K]) {
-        uint4* q = reinterpret_cast<uint4*>(p);
+    __device__ __forceinline__ static void encode(const float (&v)[K], uint4 (&w)[K / 8]) {
 #pragma unroll
         for (int k = 0; k < K / 8; ++k) {
-            uint32_t w[4];
+            uint32_t u[4];
 #pragma unroll
             for (int h = 0; h < 4; ++h)
-                w[h] = f32_to_bf16(v[8 * k + 2 * h]) | (f32_to_bf16(v[8 * k + 2 * h + 1]) << 16);
-            q[k] = make_uint4(w[0], w[1], w[2], w[3]);
+                u[h] = f32_to_bf16(v[8 * k + 2 * h]) | (f32_to_bf16(v[8 * k + 2 * h + 1]) << 16);
+            w[k] = make_uint4(u[0], u[1], u[2], u[3]);
+        }
+    }
+};
+
+// ---- movement of one matrix per lane between HBM and registers ------------
+//
+// A wave owns 64 consecutive matrices, one per lane, each C 16-byte chunks long
+// and stored back to back.
+//
+// Small matrices (C <= 4, at most 64 bytes): loading them lane by lane would
+// make every load instruction touch 64 scattered 16-byte pieces of a
+// 64*C*16-byte span, only a quarter of each 64-byte line.  Instead the wave
+// reads (and writes) the span with fully coalesced 16-byte accesses -- chunk
+// c = k*64 + lane in instruction k -- and swaps the chunks into their owners'
+// registers through a private region of LDS.  Within a matrix, chunk q sits at
+// slot q ^ f(m), f(m) = (m / (16/C)) mod C, so that the 16 lanes of any LDS
+// access phase hit 16 different 16-byte bank groups on both sides.  Only the
+// issuing wave touches its region, so ordering inside the wave needs no
+// workgroup barrier.
+//
+// Larger matrices (C >= 8, whole 128-byte lines per lane) are read and written
+// by their owners directly: every line an instruction touches is consumed in
+// full by the same lane within the next instructions, and the LDS round trip
+// would cost more registers than it saves.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int C>
+struct WaveTile {
+    static_assert(C == 2 || C == 4 || C == 8 || C == 16, "chunks per matrix");
+    static constexpr bool kStaged = C <= 4;
+    static constexpr int kLdsChunks = kStaged ? 64 * C : 1;   // LDS tile per wave, in 16-byte chunks
+    __device__ __forceinline__ static int slot(int m, int q) { return m * C + (q ^ ((m / (16 / C)) & (C - 1))); }
+    // chunk that a lane handles in access k: coalesced order when staged, its own chunk k otherwise
+    __device__ __forceinline__ static int chunk(int k, int lane) { return kStaged ? k * 64 + lane : lane * C + k; }
+
+    // Issue the global loads of one wave tile.  `src` points at the wave's first
+    // matrix; `valid` (wave-uniform, >= 1) chunks exist.  A full tile loads
+    // unconditionally; in a partial one, chunks at or beyond `valid` read the
+    // last valid chunk instead and are then zeroed.  Either way every load is
+    // issued before any is waited for.
+    __device__ __forceinline__ static void fetch(const uint4* __restrict__ src, int valid, int lane, uint4 (&t)[C]) {
+        if (valid == 64 * C) {
+#pragma unroll
+            for (int k = 0; k < C; ++k) t[k] = src[chunk(k, lane)];
+        } else {
+#pragma unroll
+            for (int k = 0; k < C; ++k) {
+                const int c = chunk(k, lane);
+                t[k] = src[c < valid ? c : valid - 1];
+            }
+#pragma unroll
+            for (int k = 0; k < C; ++k) {
+                const bool keep = chunk(k, lane) < valid;
+                t[k].x = keep ? t[k].x : 0u;
+                t[k].y = keep ? t[k].y : 0u;
+                t[k].z = keep ? t[k].z : 0u;
+                t[k].w = keep ? t[k].w : 0u;
+            }
+        }
+    }
+
+    // Fetched chunks -> registers of their owners.
+    __device__ __forceinline__ static void route(const uint4 (&t)[C], uint4* lds, int lane, uint4 (&own)[C]) {
+        if constexpr (kStaged) {
+#pragma unroll
+            for (int k = 0; k < C; ++k) {
+                const int c = chunk(k, lane);
+                lds[slot(c / C, c % C)] = t[k];
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int q = 0; q < C; ++q) own[q] = lds[slot(lane, q)];
+            wave_lds_sync();
+        } else {
+#pragma unroll
+            for (int q = 0; q < C; ++q) own[q] = t[q];
+        }
+    }
+
+    __device__ __forceinline__ static void load(const uint4* __restrict__ src, int valid, uint4* lds, int lane,
+                                                uint4 (&own)[C]) {
+        uint4 t[C];
+        fetch(src, valid, lane, t);
+        route(t, lds, lane, own);
+    }
+
+    // Registers of the owning lane -> global.  `valid` (wave-uniform) chunks
+    // exist; the rest are not written.  A full tile stores unconditionally.
+    __device__ __forceinline__ static void store(const uint4 (&own)[C], uint4* lds, int lane, uint4* __restrict__ dst,
+                                                 int valid) {
+        const bool full = valid == 64 * C;
+        if constexpr (kStaged) {
+#pragma unroll
+            for (int q = 0; q < C; ++q) lds[slot(lane, q)] = own[q];
+            wave_lds_sync();
+            if (full) {
+#pragma unroll
+                for (int k = 0; k < C; ++k) {
+                    const int c = chunk(k, lane);
+                    dst[c] = lds[slot(c / C, c % C)];
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < C; ++k) {
+                    const int c = chunk(k, lane);
+                    const uint4 v = lds[slot(c / C, c % C)];
+                    if (c < valid) dst[c] = v;
+                }
+            }
+            wave_lds_sync();
+        } else {
+            if (full) {
+#pragma unroll
+                for (int k = 0; k < C; ++k) dst[chunk(k, lane)] = own[k];
+            } else {
+#pragma unroll
+                for (int k = 0; k < C; ++k) {
+                    const int c = chunk(k, lane);
+                    if (c < valid) dst[c] = own[k];
+                }
+            }
         }
     }
 };

@@ -2,12 +2,14 @@
 // onto the Birkhoff polytope and its implicit backward pass (gfx950).
 //
 // Layout.  One matrix per lane: a wave of 64 lanes owns 64 consecutive
-// matrices, each held entirely in VGPRs (n = 4: 16 logits, 16 entries of T,
-// the 6-entry Hessian triangle).  There is no cross-lane traffic, no LDS and
-// no MFMA: the work is tiny and independent per matrix, and the per-matrix
-// scalar logic (the 3x3 solve, the step-size search) runs once per matrix
-// rather than being replicated across a group of lanes.  Control flow is
-// per lane; the wave keeps stepping while any of its lanes is unconverged.
+// matrices, each held entirely in VGPRs (n = 4: 16 entries of T and the
+// 6-entry Hessian triangle).  All arithmetic is per lane -- no cross-lane
+// reductions and no MFMA: the work is tiny and independent per matrix, and the
+// per-matrix scalar logic (the 3x3 solve, the step-size search) runs once per
+// matrix rather than being replicated across a group of lanes.  LDS is used
+// only to turn the matrix loads and stores into coalesced wave-wide accesses
+// (WaveTile).  Control flow is per lane; the wave keeps stepping while any of
+// its lanes is unconverged.
 //
 // Units.  Logits are scaled by log2(e) on load and the dual is kept in the
 // same base-2 units (y = beta * log2 e), so that every exponential is one
@@ -47,12 +49,11 @@ __device__ __forceinline__ void softmax_rows(const float (&L)[N * N], const floa
         float mu = u[0];
 #pragma unroll
         for (int j = 1; j < N; ++j) mu = fmaxf(mu, u[j]);
-        float s = 0.0f;
 #pragma unroll
-        for (int j = 0; j < N; ++j) {
-            u[j] = ex2(u[j] - mu);
-            s += u[j];
-        }
+        for (int j = 0; j < N; ++j) u[j] = ex2(u[j] - mu);
+        float s = u[0];
+#pragma unroll
+        for (int j = 1; j < N; ++j) s += u[j];
         const float r = rcp(s);
 #pragma unroll
         for (int j = 0; j < N; ++j) T[i * N + j] = u[j] * r;
@@ -103,19 +104,20 @@ __device__ __forceinline__ void hessian(const float (&T)[N * N], float (&h)[Tri<
         }
     float dg[M];
 #pragma unroll
-    for (int j = 0; j < M; ++j) dg[j] = 0.0f;
-#pragma unroll
     for (int i = 0; i < N; ++i) {
         // o_j = sum of row i without entry j, from prefix and suffix sums
-        float pre[N], suf[N];
-        pre[0] = 0.0f;
+        float pre[N], suf[N];   // pre[k] = T_i0 + .. + T_i,k-1 (k >= 1); suf[k] = T_i,k+1 + .. (k <= N-2)
+        pre[1] = T[i * N];
 #pragma unroll
-        for (int k = 1; k < N; ++k) pre[k] = (k == 1) ? T[i * N] : pre[k - 1] + T[i * N + k - 1];
-        suf[N - 1] = 0.0f;
+        for (int k = 2; k < N; ++k) pre[k] = pre[k - 1] + T[i * N + k - 1];
+        suf[N - 2] = T[i * N + N - 1];
 #pragma unroll
-        for (int k = N - 2; k >= 0; --k) suf[k] = (k == N - 2) ? T[i * N + N - 1] : suf[k + 1] + T[i * N + k + 1];
+        for (int k = N - 3; k >= 0; --k) suf[k] = suf[k + 1] + T[i * N + k + 1];
 #pragma unroll
-        for (int j = 0; j < M; ++j) dg[j] = fmaf(T[i * N + j], pre[j] + suf[j], dg[j]);
+        for (int j = 0; j < M; ++j) {
+            const float o = (j == 0) ? suf[0] : pre[j] + suf[j];
+            dg[j] = (i == 0) ? T[j] * o : fmaf(T[i * N + j], o, dg[j]);
+        }
     }
 #pragma unroll
     for (int j = 0; j < M; ++j) h[Tri<N>::at(j, j)] = dg[j];
@@ -189,28 +191,70 @@ struct SpdSolve<4> {
     }
 };
 
-// f(x + s) - f(x) for the step s (natural units, s_{N-1} = 0), by the exact identity
-//   sum_i log(sum_j T_ij e^{s_j}) - sum_j s_j
-// that follows from f = n + sum_i LSE_i(H_i. + beta) - sum_j beta_j (eq 8 with eq 5),
-// written as sum_i log1p(sum_j T_ij expm1(s_j)) - sum_j s_j so that it keeps its
-// relative accuracy when the step is small (rows of T sum to one).
+// Trial point x + s of the line search (natural units, s_{N-1} = 0), evaluated
+// from the current T instead of from the logits.  Rows of T are softmaxes of
+// H_i. + beta, so moving beta by s multiplies column j by e^{s_j} before the
+// rows are normalised again:
+//     T'_ij = (T_ij e^{s_j}) r_i,   r_i = 1 / sum_k T_ik e^{s_k}     (N-1 exponentials, not N^2).
+// The same row sums give the change of the objective by the exact identity
+//     f(x + s) - f(x) = sum_i log(sum_j T_ij e^{s_j}) - sum_j s_j,
+// which follows from f = n + sum_i LSE_i(H_i. + beta) - sum_j beta_j (eq 8 with
+// eq 5).  For a small step the sum of logarithms nearly cancels the sum of
+// steps, so it is taken as log1p(q), q = prod_i (1 + a_i) - 1 with
+// a_i = sum_j T_ij expm1(s_j) (rows of T sum to one), accumulated as
+// q <- q + a_i + q a_i, which keeps its relative accuracy as the step shrinks.
+// Otherwise (|q| >= 1/16) the logarithms of the row sums themselves are added.
+// T' itself is not formed: the column sums ct of T' (for the gradient
+// test) are accumulated row by row, and e, r are returned so that an accepted
+// trial is applied to T in place by accept_trial.  Returns f(x + s) - f(x).
 template <int N>
-__device__ __forceinline__ float objective_change(const float (&T)[N * N], const float (&s)[N - 1]) {
-    float em[N - 1];
-    float df = 0.0f;
+__device__ __forceinline__ float trial_point(const float (&T)[N * N], const float (&s)[N - 1], float (&e)[N - 1],
+                                             float (&r)[N], float (&ct)[N]) {
+    constexpr int M = N - 1;
+    float em[M];
+    float ssum = s[0];
 #pragma unroll
-    for (int j = 0; j < N - 1; ++j) {
-        em[j] = expm1_from(s[j], ex2(s[j] * kLog2e));
-        df -= s[j];
+    for (int j = 0; j < M; ++j) {
+        e[j] = ex2(s[j] * kLog2e);
+        em[j] = expm1_from(s[j], e[j]);
+        if (j > 0) ssum += s[j];
     }
+    float q = 0.0f;   // prod_i (1 + a_i) - 1
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        float a = T[i * N] * em[0];
+        float t = T[i * N] * em[0];
 #pragma unroll
-        for (int j = 1; j < N - 1; ++j) a = fmaf(T[i * N + j], em[j], a);
-        df += log1p_acc(a);
+        for (int j = 1; j < M; ++j) t = fmaf(T[i * N + j], em[j], t);
+        q = fmaf(q, t, q + t);
     }
-    return df;
+    float lsum = 0.0f;   // sum_i log2(rs_i), used when the step is not small
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        float u[M];
+        float rs = T[i * N + M];
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+            u[j] = T[i * N + j] * e[j];
+            rs += u[j];
+        }
+        r[i] = rcp(rs);
+        lsum = (i == 0) ? lg2(rs) : lsum + lg2(rs);
+#pragma unroll
+        for (int j = 0; j < M; ++j) ct[j] = (i == 0) ? u[j] * r[i] : ct[j] + u[j] * r[i];
+        ct[M] = (i == 0) ? T[i * N + M] * r[i] : ct[M] + T[i * N + M] * r[i];
+    }
+    return (fabsf(q) < 0.0625f ? log1p_series(q) : lsum * kLn2) - ssum;
+}
+
+template <int N>
+__device__ __forceinline__ void accept_trial(float (&T)[N * N], const float (&e)[N - 1], const float (&r)[N]) {
+    constexpr int M = N - 1;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+#pragma unroll
+        for (int j = 0; j < M; ++j) T[i * N + j] = (T[i * N + j] * e[j]) * r[i];
+        T[i * N + M] *= r[i];
+    }
 }
 
 // One Sinkhorn-Knopp sweep in the log domain (eq 7 = eq 2), used as the fallback
@@ -230,9 +274,9 @@ __device__ __forceinline__ void sinkhorn_sweep(const float (&L)[N * N], float (&
         float mu = u[0];
 #pragma unroll
         for (int j = 1; j < N; ++j) mu = fmaxf(mu, u[j]);
-        float s = 0.0f;
+        float s = ex2(u[0] - mu);
 #pragma unroll
-        for (int j = 0; j < N; ++j) s += ex2(u[j] - mu);
+        for (int j = 1; j < N; ++j) s += ex2(u[j] - mu);
         a[i] = -(mu + lg2(s));
     }
     float z[N];
@@ -244,9 +288,9 @@ __device__ __forceinline__ void sinkhorn_sweep(const float (&L)[N * N], float (&
         float m = v[0];
 #pragma unroll
         for (int i = 1; i < N; ++i) m = fmaxf(m, v[i]);
-        float s = 0.0f;
+        float s = ex2(v[0] - m);
 #pragma unroll
-        for (int i = 0; i < N; ++i) s += ex2(v[i] - m);
+        for (int i = 1; i < N; ++i) s += ex2(v[i] - m);
         z[j] = -(m + lg2(s));
     }
 #pragma unroll
@@ -259,6 +303,69 @@ __device__ __forceinline__ float step_size(int k) {
 }
 
 // ---------------------------------------------------------------------------
+// Kernel geometry.  A workgroup is kBlock lanes = kWaves waves; wave w of
+// workgroup g owns matrices [(g*kWaves + w)*64, +64), one per lane.  Matrix
+// I/O goes through the wave's private LDS tile (WaveTile), so every global
+// access instruction is fully coalesced; the dual (n floats per matrix) and
+// the iteration counts are already contiguous across lanes and are accessed
+// directly.  Lanes past the end of the batch compute on zeros and store
+// nothing; whole waves past the end return at once.
+// ---------------------------------------------------------------------------
+constexpr int kWaves = kBlock / 64;
+
+template <int N, typename IO>
+struct Geometry {
+    static constexpr int C = N * N * (int)sizeof(IO) / 16;   // 16-byte chunks per matrix
+    static_assert(C * 16 == N * N * (int)sizeof(IO), "matrix must be a whole number of 16-byte chunks");
+    using Tile = WaveTile<C>;
+    int lane, wave, nvalid;
+    int64_t base;   // first matrix of this wave
+    __device__ __forceinline__ Geometry(int64_t B) {
+        lane = threadIdx.x & 63;
+        wave = threadIdx.x >> 6;
+        base = ((int64_t)blockIdx.x * kWaves + wave) * 64;
+        const int64_t left = B - base;
+        nvalid = __builtin_amdgcn_readfirstlane(left <= 0 ? 0 : left >= 64 ? 64 : (int)left);   // wave-uniform
+    }
+    __device__ __forceinline__ const uint4* chunks(const IO* p) const {
+        return reinterpret_cast<const uint4*>(p) + base * C;
+    }
+    __device__ __forceinline__ uint4* chunks(IO* p) const { return reinterpret_cast<uint4*>(p) + base * C; }
+};
+
+template <int N>
+__device__ __forceinline__ void store_dual(float* __restrict__ dual, int64_t b, const float (&beta)[N]) {
+    float4* q = reinterpret_cast<float4*>(dual + b * N);
+#pragma unroll
+    for (int k = 0; k < N / 4; ++k) q[k] = make_float4(beta[4 * k], beta[4 * k + 1], beta[4 * k + 2], beta[4 * k + 3]);
+}
+
+template <int N>
+__device__ __forceinline__ void load_dual(const float* __restrict__ dual, int64_t b, float (&beta)[N]) {
+    const float4* q = reinterpret_cast<const float4*>(dual + b * N);
+#pragma unroll
+    for (int k = 0; k < N / 4; ++k) {
+        const float4 t = q[k];
+        beta[4 * k] = t.x;
+        beta[4 * k + 1] = t.y;
+        beta[4 * k + 2] = t.z;
+        beta[4 * k + 3] = t.w;
+    }
+}
+
+// One lane reads its own matrix directly (used off the main path, where the
+// other lanes of the wave do not take part).
+template <int N, typename IO>
+__device__ __forceinline__ void load_own(const IO* __restrict__ p, int64_t b, float (&v)[N * N]) {
+    constexpr int C = N * N * (int)sizeof(IO) / 16;
+    const uint4* q = reinterpret_cast<const uint4*>(p) + b * C;
+    uint4 w[C];
+#pragma unroll
+    for (int k = 0; k < C; ++k) w[k] = q[k];
+    Storage<IO>::template decode<N * N>(w, v);
+}
+
+// ---------------------------------------------------------------------------
 // Forward: Newton on the reduced dual (eq 8), one matrix per lane.
 // ---------------------------------------------------------------------------
 template <int N, typename IO, bool kStats>
@@ -266,21 +373,30 @@ __global__ void __launch_bounds__(kBlock)
 newton_fwd_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, float* __restrict__ dual,
                   int32_t* __restrict__ iters, int64_t B, float tol, int max_iter) {
     constexpr int M = N - 1;
-    const int64_t b = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (b >= B) return;
+    using G = Geometry<N, IO>;
+    __shared__ uint4 lds[kWaves][G::Tile::kLdsChunks];
+    const G geo(B);
+    if (geo.nvalid == 0) return;
+    const bool valid = geo.lane < geo.nvalid;
+    const int64_t b = geo.base + geo.lane;
 
-    float L[N * N];
-    Storage<IO>::template load<N * N>(logits + b * (N * N), L);
-#pragma unroll
-    for (int k = 0; k < N * N; ++k) L[k] *= kLog2e;
-
+    // The logits are needed again only by the rare fallback sweep, which
+    // re-reads them; they do not stay in registers through the loop.
+    float T[N * N], c[N];
     float y[M];
 #pragma unroll
     for (int j = 0; j < M; ++j) y[j] = 0.0f;   // x^(0) = 0
-    float T[N * N], c[N];
-    softmax_rows<N>(L, y, T);
+    {
+        float L[N * N];
+        uint4 w[G::C];
+        G::Tile::load(geo.chunks(logits), geo.nvalid * G::C, lds[geo.wave], geo.lane, w);
+        Storage<IO>::template decode<N * N>(w, L);
+#pragma unroll
+        for (int k = 0; k < N * N; ++k) L[k] *= kLog2e;
+        softmax_rows<N>(L, y, T);
+    }
     col_sums<N>(T, c);
-    float res = col_residual<N>(c);
+    float res = valid ? col_residual<N>(c) : 0.0f;
     int it = 0;
 
     while (res > tol && it < max_iter) {
@@ -300,24 +416,17 @@ newton_fwd_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, float* _
         if (ok) {
             for (int k = 0; k < 5; ++k) {
                 const float gam = step_size(k);
-                float s[M], yt[M];
+                float s[M], e[M], rr[N], ct[N];
 #pragma unroll
-                for (int j = 0; j < M; ++j) {
-                    s[j] = gam * d[j];
-                    yt[j] = fmaf(s[j], kLog2e, y[j]);
-                }
-                const float df = objective_change<N>(T, s);
-                float Tt[N * N], ct[N];
-                softmax_rows<N>(L, yt, Tt);
-                col_sums<N>(Tt, ct);
+                for (int j = 0; j < M; ++j) s[j] = gam * d[j];
+                const float df = trial_point<N>(T, s, e, rr, ct);
                 float gt2 = 0.0f;
 #pragma unroll
                 for (int j = 0; j < M; ++j) gt2 = fmaf(ct[j] - 1.0f, ct[j] - 1.0f, gt2);
                 if (df < 0.0f && gt2 < gn2) {
 #pragma unroll
-                    for (int j = 0; j < M; ++j) y[j] = yt[j];
-#pragma unroll
-                    for (int q = 0; q < N * N; ++q) T[q] = Tt[q];
+                    for (int j = 0; j < M; ++j) y[j] = fmaf(s[j], kLog2e, y[j]);
+                    accept_trial<N>(T, e, rr);
 #pragma unroll
                     for (int j = 0; j < N; ++j) c[j] = ct[j];
                     accepted = true;
@@ -326,6 +435,10 @@ newton_fwd_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, float* _
             }
         }
         if (!accepted) {
+            float L[N * N];
+            load_own<N, IO>(logits, b, L);
+#pragma unroll
+            for (int k = 0; k < N * N; ++k) L[k] *= kLog2e;
             sinkhorn_sweep<N>(L, y);
             softmax_rows<N>(L, y, T);
             col_sums<N>(T, c);
@@ -334,30 +447,55 @@ newton_fwd_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, float* _
         res = col_residual<N>(c);
     }
 
-    Storage<IO>::template store<N * N>(Tout + b * (N * N), T);
-    float beta[N];
+    {
+        uint4 w[G::C];
+        Storage<IO>::template encode<N * N>(T, w);
+        G::Tile::store(w, lds[geo.wave], geo.lane, geo.chunks(Tout), geo.nvalid * G::C);
+    }
+    if (valid) {
+        float beta[N];
 #pragma unroll
-    for (int j = 0; j < M; ++j) beta[j] = y[j] * kLn2;
-    beta[M] = 0.0f;
-    Storage<float>::template store<N>(dual + b * N, beta);
-    if (kStats) iters[b] = (res <= tol) ? it : -1;
+        for (int j = 0; j < M; ++j) beta[j] = y[j] * kLn2;
+        beta[M] = 0.0f;
+        store_dual<N>(dual, b, beta);
+        if (kStats) iters[b] = (res <= tol) ? it : -1;
+    }
 }
 
 // ---------------------------------------------------------------------------
 // Backward: eq (13) at T recomputed from (logits, dual), one matrix per lane.
 // ---------------------------------------------------------------------------
 template <int N, typename IO>
-__global__ void __launch_bounds__(kBlock)
+__global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(N == 4 ? 8 : 1)))
 implicit_bwd_kernel(const IO* __restrict__ logits, const float* __restrict__ dual, const IO* __restrict__ dT,
                     IO* __restrict__ dH, int64_t B) {
     constexpr int M = N - 1;
-    const int64_t b = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (b >= B) return;
+    using Gm = Geometry<N, IO>;
+    constexpr int C = Gm::C;
+    __shared__ uint4 lds[kWaves][Gm::Tile::kLdsChunks];
+    const Gm geo(B);
+    if (geo.nvalid == 0) return;
+    const bool valid = geo.lane < geo.nvalid;
+    const int64_t b = geo.base + geo.lane;
 
-    float L[N * N], G[N * N], beta[N];
-    Storage<IO>::template load<N * N>(logits + b * (N * N), L);
-    Storage<float>::template load<N>(dual + b * N, beta);
-    Storage<IO>::template load<N * N>(dT + b * (N * N), G);
+    // issue every global load first, then route the chunks to their owners
+    uint4 th[C], tg[C];
+    Gm::Tile::fetch(geo.chunks(logits), geo.nvalid * C, geo.lane, th);
+    Gm::Tile::fetch(geo.chunks(dT), geo.nvalid * C, geo.lane, tg);
+    float beta[N];
+    if (valid)
+        load_dual<N>(dual, b, beta);
+    else
+#pragma unroll
+        for (int j = 0; j < N; ++j) beta[j] = 0.0f;
+    float L[N * N], G[N * N];
+    {
+        uint4 w[C];
+        Gm::Tile::route(th, lds[geo.wave], geo.lane, w);
+        Storage<IO>::template decode<N * N>(w, L);
+        Gm::Tile::route(tg, lds[geo.wave], geo.lane, w);
+        Storage<IO>::template decode<N * N>(w, G);
+    }
 #pragma unroll
     for (int k = 0; k < N * N; ++k) L[k] *= kLog2e;
     float y[M];
@@ -400,7 +538,11 @@ implicit_bwd_kernel(const IO* __restrict__ logits, const float* __restrict__ dua
             out[i * N + j] = (G[i * N + j] - v - wj) * T[i * N + j];
         }
     }
-    Storage<IO>::template store<N * N>(dH + b * (N * N), out);
+    {
+        uint4 wo[C];
+        Storage<IO>::template encode<N * N>(out, wo);
+        Gm::Tile::store(wo, lds[geo.wave], geo.lane, geo.chunks(dH), geo.nvalid * C);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -409,10 +551,16 @@ implicit_bwd_kernel(const IO* __restrict__ logits, const float* __restrict__ dua
 template <int N, typename IO>
 __global__ void __launch_bounds__(kBlock)
 sinkhorn_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, int64_t B, int sweeps) {
-    const int64_t b = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (b >= B) return;
+    using G = Geometry<N, IO>;
+    __shared__ uint4 lds[kWaves][G::Tile::kLdsChunks];
+    const G geo(B);
+    if (geo.nvalid == 0) return;
     float L[N * N];
-    Storage<IO>::template load<N * N>(logits + b * (N * N), L);
+    {
+        uint4 w[G::C];
+        G::Tile::load(geo.chunks(logits), geo.nvalid * G::C, lds[geo.wave], geo.lane, w);
+        Storage<IO>::template decode<N * N>(w, L);
+    }
 #pragma unroll
     for (int k = 0; k < N * N; ++k) L[k] *= kLog2e;
     float a[N], z[N];
@@ -430,9 +578,9 @@ sinkhorn_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, int64_t B,
             float mu = u[0];
 #pragma unroll
             for (int j = 1; j < N; ++j) mu = fmaxf(mu, u[j]);
-            float s = 0.0f;
+            float s = ex2(u[0] - mu);
 #pragma unroll
-            for (int j = 0; j < N; ++j) s += ex2(u[j] - mu);
+            for (int j = 1; j < N; ++j) s += ex2(u[j] - mu);
             a[i] = -(mu + lg2(s));
         }
 #pragma unroll
@@ -443,9 +591,9 @@ sinkhorn_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, int64_t B,
             float m = v[0];
 #pragma unroll
             for (int i = 1; i < N; ++i) m = fmaxf(m, v[i]);
-            float s = 0.0f;
+            float s = ex2(v[0] - m);
 #pragma unroll
-            for (int i = 0; i < N; ++i) s += ex2(v[i] - m);
+            for (int i = 1; i < N; ++i) s += ex2(v[i] - m);
             z[j] = -(m + lg2(s));
         }
     }
@@ -454,7 +602,11 @@ sinkhorn_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, int64_t B,
     for (int i = 0; i < N; ++i)
 #pragma unroll
         for (int j = 0; j < N; ++j) T[i * N + j] = ex2(L[i * N + j] + a[i] + z[j]);
-    Storage<IO>::template store<N * N>(Tout + b * (N * N), T);
+    {
+        uint4 w[G::C];
+        Storage<IO>::template encode<N * N>(T, w);
+        G::Tile::store(w, lds[geo.wave], geo.lane, geo.chunks(Tout), geo.nvalid * G::C);
+    }
 }
 
 }  // namespace birk
