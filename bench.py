@@ -7,21 +7,32 @@ matrix of the workload.  The default workload is the training-shaped mHC pass:
 B = 16 sequences x 4096 tokens x 32 layers = 2,097,152 matrices of 4x4 fp32
 logits H = N(0, 0.5^2) + 2I with upstream dL/dT = N(0, 0.1^2), tol 1e-6.
 
-Inputs are generated on the host from fixed seeds, copied to HBM before the
-timed region, and two input/output sets alternate between steps so that a
-step never finds the previous step's data in the 256 MB last-level cache.
+Inputs are generated on the host from fixed seeds and copied to HBM before
+anything is timed.  Two complete input/output sets alternate between steps, so
+that a step never finds the previous step's data in the 256 MB last-level
+cache.  The timed region is `--steps` back-to-back steps between two HIP events
+on the stream the kernels run on; `value` is B / (time per step).
 
-Prints one JSON line.  Per-kernel durations come from HIP events recorded on
-the stream the kernels run on; the roofline figure uses algorithmic bytes
-(each input read once, each output written once).  The CPU baseline is the
-float64 oracle timed on a bounded sample of the same workload.
+The roofline figure is for the kernel with the longer average launch time.
+Each kernel's average launch time is measured separately, right after the
+timed region, as `--steps` back-to-back launches of that kernel alone
+(alternating the two sets) between two HIP events on the same stream --
+events between the two kernels of a step would themselves add gaps.
+`achieved` divides the kernel's algorithmic bytes per launch (each input read
+once, each output written once) by that time.  `traffic` is the HBM traffic per
+launch that rocprofv3's FETCH_SIZE / WRITE_SIZE counters measured for the same
+kernel sources (profiles/traffic_<workload>.json), or null when the kernels
+have changed since.
+
+The CPU baseline is the float64 oracle timed on a bounded sample of the same
+workload on this host's cores.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload train]
 """
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
-import os
 import pathlib
 import sys
 import time
@@ -31,14 +42,6 @@ sys.path.insert(0, str(ROOT))
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak, GB/s
 METRIC = "4x4 Birkhoff projections/sec (fwd+bwd, fp32) on 1 MI355X; % HBM roofline"
-
-
-def kernel_source_digest() -> str:
-    h = hashlib.sha256()
-    for p in sorted((ROOT / "birkhoff_projection_amd" / "csrc").glob("*")):
-        h.update(p.name.encode())
-        h.update(p.read_bytes())
-    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str, kernel: str, digest: str):
@@ -56,7 +59,6 @@ def measured_traffic(workload: str, kernel: str, digest: str):
 def cpu_baseline(w, target_s: float = 10.0):
     """The float64 oracle (reference projection + eq (13) backward) on a bounded
     sample of the workload, on this host's cores."""
-    import numpy as np
     import oracle
     from birkhoff_projection_amd import workloads as W
 
@@ -73,8 +75,9 @@ def cpu_baseline(w, target_s: float = 10.0):
     Bs = int(min(w.B, max(probe, probe * target_s / max(dt, 1e-6))))
     dt = run(Bs)
     return {"value": Bs / dt, "unit": "projections/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": "first %d matrices of the same seeded workload (float64 Sinkhorn to 1e-13 with a "
-                      "Newton cross-check, then the eq (13) backward), %.1f s wall" % (Bs, dt)}
+            "sample": "the first %d matrices of the same seeded workload (%s), float64: Sinkhorn to 1e-13 "
+                      "with a Newton cross-check, then the eq (13) backward; %.1f s wall"
+                      % (Bs, "all of it" if Bs == w.B else "a prefix", dt)}
 
 
 def main() -> int:
@@ -85,6 +88,9 @@ def main() -> int:
     ap.add_argument("--workload", default="train", help="workload key (train is the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="after the timed steps, run 5 torch copies of MIB MiB (fp32) so that a counter "
+                         "run can scale FETCH_SIZE / WRITE_SIZE against a copy of known size")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -93,10 +99,10 @@ def main() -> int:
               "--gpus %d is not supported" % args.gpus, file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     import birkhoff_projection_amd as bp
+    from birkhoff_projection_amd import build as hipbuild
     from birkhoff_projection_amd import workloads as W
 
     w = W.WORKLOADS[args.workload]
@@ -127,34 +133,36 @@ def main() -> int:
     bwd = bp.birkhoff_bwd if w.io == "f32" else bp.birkhoff_bwd_bf16
     stream = torch.cuda.current_stream(dev)
 
-    def step(s, ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def run_fwd(s):
         fwd(s["H"], s["T"], s["dual"], w.tol, w.max_iter, stream)
-        if ev is not None:
-            ev[1].record(stream)
+
+    def run_bwd(s):
         bwd(s["H"], s["dual"], s["G"], s["dH"], stream)
-        if ev is not None:
-            ev[2].record(stream)
+
+    def step(s):
+        run_fwd(s)
+        run_bwd(s)
+
+    def timed(fn, K):
+        """K launches of fn (alternating the two sets) between two events; ms per launch."""
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(K):
+            fn(sets[i % 2])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
 
     for i in range(args.warmup):
         step(sets[i % 2])
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(K):
-        step(sets[i % 2], evs[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_step = total_ms / K
-    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / K
-    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / K
+    ms_step = timed(step, K)             # the timed region: K whole steps
+    fwd_ms = timed(run_fwd, K)           # per-kernel launch times, same stream
+    bwd_ms = timed(run_bwd, K)
 
     b_fwd = W.bytes_per_projection(n, w.io, "fwd") * B
     b_bwd = W.bytes_per_projection(n, w.io, "bwd") * B
@@ -162,7 +170,7 @@ def main() -> int:
     dom = max(kern, key=lambda k: kern[k][0])
     d_ms, d_bytes = kern[dom]
     achieved = d_bytes / (d_ms * 1e-3) / 1e9
-    digest = kernel_source_digest()
+    digest = hipbuild.kernel_source_digest()
     traffic = measured_traffic(w.key, dom, digest)
 
     out = {
@@ -181,13 +189,22 @@ def main() -> int:
         "config": {"workload": "%s: %s" % (w.key, w.title), "B": B, "n": n, "storage": w.io,
                    "passes": "fwd+bwd", "tol": w.tol, "max_iter": w.max_iter},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": d_bytes, "avg_launch_ms": d_ms},
         "kernels_ms": {"birkhoff_fwd": fwd_ms, "birkhoff_bwd": bwd_ms},
         "step_hbm": {"algorithmic_bytes": b_fwd + b_bwd,
                      "achieved_GBs": (b_fwd + b_bwd) / (ms_step * 1e-3) / 1e9,
                      "frac": (b_fwd + b_bwd) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "kernel_digest": digest,
     }
+    if args.calibrate_copy > 0:
+        src = torch.ones(args.calibrate_copy << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": src.numel() * 4}
+        del src, dst
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -22,6 +22,18 @@ SOURCES = [CSRC / "birkhoff.hip"]
 ARCH = "gfx950"
 
 
+def kernel_source_digest() -> str:
+    """Short hash of every device / ABI source file; identifies which kernels a
+    profile was taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    for p in sorted(list(CSRC.glob("*")) + [ROOT / "include" / "birkhoff.h"]):
+        if p.is_file():
+            h.update(p.name.encode())
+            h.update(p.read_bytes())
+    return h.hexdigest()[:16]
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
