@@ -1,11 +1,14 @@
 #!/usr/bin/env python3
 """Benchmark: 4x4 Birkhoff projections per second (forward + backward, fp32) on one MI355X.
 
-One step = the whole hot path over one batch: birkhoff_fwd (Newton projection)
-followed by birkhoff_bwd (implicit backward) on the same stream, for every
-matrix of the workload.  The default workload is the training-shaped mHC pass:
-B = 16 sequences x 4096 tokens x 32 layers = 2,097,152 matrices of 4x4 fp32
-logits H = N(0, 0.5^2) + 2I with upstream dL/dT = N(0, 0.1^2), tol 1e-6.
+One step = the whole hot path over one batch: the Newton projection and the
+implicit backward for every matrix of the workload.  The default workload is
+the training-shaped mHC pass -- B = 16 sequences x 4096 tokens x 32 layers =
+2,097,152 matrices of 4x4 fp32 logits H = N(0, 0.5^2) + 2I with upstream
+dL/dT = N(0, 0.1^2), tol 1e-6 -- whose forward and backward are fused.  The
+timed step is therefore one birkhoff_fwd_bwd launch (--path fused, default);
+--path separate times birkhoff_fwd followed by birkhoff_bwd instead.  Either
+way the other form is timed too and reported under "other_path".
 
 Inputs are generated on the host from fixed seeds and copied to HBM before
 anything is timed.  Two complete input/output sets alternate between steps, so
@@ -13,21 +16,21 @@ that a step never finds the previous step's data in the 256 MB last-level
 cache.  The timed region is `--steps` back-to-back steps between two HIP events
 on the stream the kernels run on; `value` is B / (time per step).
 
-The roofline figure is for the kernel with the longer average launch time.
-Each kernel's average launch time is measured separately, right after the
-timed region, as `--steps` back-to-back launches of that kernel alone
-(alternating the two sets) between two HIP events on the same stream --
-events between the two kernels of a step would themselves add gaps.
+The roofline figure is for the kernel with the longer average launch time
+(the fused kernel is the only one of its step).  Each separate kernel's
+average launch time is measured as `--steps` back-to-back launches of that
+kernel alone (alternating the two sets) between two HIP events on the same
+stream -- events between the two kernels of a step would themselves add gaps.
 `achieved` divides the kernel's algorithmic bytes per launch (each input read
-once, each output written once) by that time.  `traffic` is the HBM traffic per
-launch that rocprofv3's FETCH_SIZE / WRITE_SIZE counters measured for the same
-kernel sources (profiles/traffic_<workload>.json), or null when the kernels
-have changed since.
+once, each output written once) by that time.  `traffic` is the HBM traffic
+per launch that rocprofv3's FETCH_SIZE / WRITE_SIZE counters measured for the
+same kernel sources (profiles/traffic_<workload>.json), or null when the
+kernels have changed since.
 
 The CPU baseline is the float64 oracle timed on a bounded sample of the same
 workload on this host's cores.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload train]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload train] [--path fused|separate]
 """
 from __future__ import annotations
 
@@ -88,6 +91,9 @@ def main() -> int:
     ap.add_argument("--workload", default="train", help="workload key (train is the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--path", choices=("fused", "separate"), default="fused",
+                    help="the timed step: one birkhoff_fwd_bwd launch (fused) or birkhoff_fwd then "
+                         "birkhoff_bwd (separate); the other is measured and reported alongside")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run 5 torch copies of MIB MiB (fp32) so that a counter "
                          "run can scale FETCH_SIZE / WRITE_SIZE against a copy of known size")
@@ -131,6 +137,7 @@ def main() -> int:
 
     fwd = bp.birkhoff_fwd if w.io == "f32" else bp.birkhoff_fwd_bf16
     bwd = bp.birkhoff_bwd if w.io == "f32" else bp.birkhoff_bwd_bf16
+    fused = bp.birkhoff_fwd_bwd if w.io == "f32" else bp.birkhoff_fwd_bwd_bf16
     stream = torch.cuda.current_stream(dev)
 
     def run_fwd(s):
@@ -139,9 +146,14 @@ def main() -> int:
     def run_bwd(s):
         bwd(s["H"], s["dual"], s["G"], s["dH"], stream)
 
-    def step(s):
+    def run_fused(s):
+        fused(s["H"], s["G"], s["T"], s["dual"], s["dH"], w.tol, w.max_iter, stream)
+
+    def step_separate(s):
         run_fwd(s)
         run_bwd(s)
+
+    step = run_fused if args.path == "fused" else step_separate
 
     def timed(fn, K):
         """K launches of fn (alternating the two sets) between two events; ms per launch."""
@@ -161,14 +173,22 @@ def main() -> int:
 
     K = args.steps
     ms_step = timed(step, K)             # the timed region: K whole steps
+    other = step_separate if args.path == "fused" else run_fused
+    ms_other = timed(other, K)           # the other form of the step, for comparison
     fwd_ms = timed(run_fwd, K)           # per-kernel launch times, same stream
     bwd_ms = timed(run_bwd, K)
+    fused_ms = ms_step if args.path == "fused" else ms_other
 
     b_fwd = W.bytes_per_projection(n, w.io, "fwd") * B
     b_bwd = W.bytes_per_projection(n, w.io, "bwd") * B
-    kern = {"birkhoff_fwd": (fwd_ms, b_fwd), "birkhoff_bwd": (bwd_ms, b_bwd)}
+    b_fused = W.bytes_per_projection(n, w.io, "fused") * B
+    if args.path == "fused":
+        kern = {"birkhoff_fwd_bwd": (fused_ms, b_fused)}
+    else:
+        kern = {"birkhoff_fwd": (fwd_ms, b_fwd), "birkhoff_bwd": (bwd_ms, b_bwd)}
     dom = max(kern, key=lambda k: kern[k][0])
     d_ms, d_bytes = kern[dom]
+    step_bytes = b_fused if args.path == "fused" else b_fwd + b_bwd
     achieved = d_bytes / (d_ms * 1e-3) / 1e9
     digest = hipbuild.kernel_source_digest()
     traffic = measured_traffic(w.key, dom, digest)
@@ -187,14 +207,16 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "%s: %s" % (w.key, w.title), "B": B, "n": n, "storage": w.io,
-                   "passes": "fwd+bwd", "tol": w.tol, "max_iter": w.max_iter},
+                   "passes": "fwd+bwd", "path": args.path, "tol": w.tol, "max_iter": w.max_iter},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": d_bytes, "avg_launch_ms": d_ms},
-        "kernels_ms": {"birkhoff_fwd": fwd_ms, "birkhoff_bwd": bwd_ms},
-        "step_hbm": {"algorithmic_bytes": b_fwd + b_bwd,
-                     "achieved_GBs": (b_fwd + b_bwd) / (ms_step * 1e-3) / 1e9,
-                     "frac": (b_fwd + b_bwd) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "kernels_ms": {"birkhoff_fwd_bwd": fused_ms, "birkhoff_fwd": fwd_ms, "birkhoff_bwd": bwd_ms},
+        "step_hbm": {"algorithmic_bytes": step_bytes,
+                     "achieved_GBs": step_bytes / (ms_step * 1e-3) / 1e9,
+                     "frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "other_path": {"path": "separate" if args.path == "fused" else "fused", "ms_per_step": ms_other,
+                       "value": B / (ms_other * 1e-3)},
         "kernel_digest": digest,
     }
     if args.calibrate_copy > 0:

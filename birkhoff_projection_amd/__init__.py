@@ -21,8 +21,9 @@ from typing import Optional
 __all__ = [
     "BirkhoffError", "library_path", "load_library",
     "birkhoff_fwd", "birkhoff_fwd_ex", "birkhoff_bwd", "sinkhorn_fwd",
-    "birkhoff_fwd_bf16", "birkhoff_bwd_bf16", "birkhoff_strerror", "birkhoff_abi_version",
-    "project", "project_bwd", "sinkhorn", "BirkhoffProjection",
+    "birkhoff_fwd_bf16", "birkhoff_bwd_bf16", "birkhoff_fwd_bwd", "birkhoff_fwd_bwd_bf16",
+    "birkhoff_strerror", "birkhoff_abi_version",
+    "project", "project_bwd", "project_fwd_bwd", "sinkhorn", "BirkhoffProjection",
 ]
 
 _PKG = pathlib.Path(__file__).resolve().parent
@@ -59,6 +60,8 @@ def load_library():
         "sinkhorn_fwd": [vp, vp, i64, ci, ci, vp],
         "birkhoff_fwd_bf16": [vp, vp, vp, i64, ci, cf, ci, vp],
         "birkhoff_bwd_bf16": [vp, vp, vp, vp, i64, ci, vp],
+        "birkhoff_fwd_bwd": [vp, vp, vp, vp, vp, i64, ci, cf, ci, vp],
+        "birkhoff_fwd_bwd_bf16": [vp, vp, vp, vp, vp, i64, ci, cf, ci, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -221,6 +224,34 @@ def birkhoff_bwd_bf16(logits, dual, dT, dH, stream=None) -> None:
     _call("birkhoff_bwd_bf16", dev, _p(logits), _p(dual), _p(dT), _p(dH), B, n, _stream_handle(stream, dev))
 
 
+def birkhoff_fwd_bwd(logits, dT, T, dual, dH, tol: float = 1e-6, max_iter: int = 50, stream=None) -> None:
+    """Forward and backward in one launch (fp32): T, dual as birkhoff_fwd; dH = dL/dlogits for dT."""
+    torch = _torch()
+    _mats(logits, "logits", torch.float32)
+    B, n = logits.shape[0], logits.shape[1]
+    _mats(dT, "dT", torch.float32, B, n)
+    _mats(T, "T", torch.float32, B, n)
+    _vec(dual, "dual", B, n, torch.float32)
+    _mats(dH, "dH", torch.float32, B, n)
+    dev = _same_device(logits, dT, T, dual, dH)
+    _call("birkhoff_fwd_bwd", dev, _p(logits), _p(dT), _p(T), _p(dual), _p(dH), B, n, float(tol), int(max_iter),
+          _stream_handle(stream, dev))
+
+
+def birkhoff_fwd_bwd_bf16(logits, dT, T, dual, dH, tol: float = 1e-6, max_iter: int = 50, stream=None) -> None:
+    """Forward and backward in one launch with bf16 storage (fp32 arithmetic and fp32 dual)."""
+    torch = _torch()
+    _bf16_mats(logits, "logits")
+    B, n = logits.shape[0], logits.shape[1]
+    _bf16_mats(dT, "dT", B, n)
+    _bf16_mats(T, "T", B, n)
+    _vec(dual, "dual", B, n, torch.float32)
+    _bf16_mats(dH, "dH", B, n)
+    dev = _same_device(logits, dT, T, dual, dH)
+    _call("birkhoff_fwd_bwd_bf16", dev, _p(logits), _p(dT), _p(T), _p(dual), _p(dH), B, n, float(tol),
+          int(max_iter), _stream_handle(stream, dev))
+
+
 # ------------------------------------------------------- allocating helpers
 
 def project(logits, tol: float = 1e-6, max_iter: int = 50, stream=None):
@@ -245,6 +276,20 @@ def project_bwd(logits, dual, dT, stream=None):
     else:
         birkhoff_bwd_bf16(logits, dual, dT, dH, stream)
     return dH
+
+
+def project_fwd_bwd(logits, dT, tol: float = 1e-6, max_iter: int = 50, stream=None):
+    """Allocate outputs and run forward + backward in one launch. Returns (T, dual, dH)."""
+    torch = _torch()
+    B, n = logits.shape[0], logits.shape[1]
+    dual = torch.empty((B, n), dtype=torch.float32, device=logits.device)
+    T = torch.empty_like(logits, memory_format=torch.contiguous_format)
+    dH = torch.empty_like(dT, memory_format=torch.contiguous_format)
+    if logits.dtype == torch.float32:
+        birkhoff_fwd_bwd(logits, dT, T, dual, dH, tol, max_iter, stream)
+    else:
+        birkhoff_fwd_bwd_bf16(logits, dT, T, dual, dH, tol, max_iter, stream)
+    return T, dual, dH
 
 
 def sinkhorn(logits, iters: int = 20, stream=None):

@@ -88,6 +88,24 @@ int bwd_entry(const IO* logits, const float* dual, const IO* dT, IO* dH, int64_t
     return launched();
 }
 
+template <typename IO>
+int fused_entry(const IO* logits, const IO* dT, IO* T, float* dual, IO* dH, int64_t B, int n, float tol,
+                int max_iter, void* stream) {
+    int rc = check_batch(B, n);
+    if (rc == BIRKHOFF_OK) rc = check_tol(tol, max_iter);
+    if (rc != BIRKHOFF_OK || B == 0) return rc;
+    rc = check_ptrs({logits, dT, T, dual, dH});
+    if (rc != BIRKHOFF_OK) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (n == 4)
+        hipLaunchKernelGGL((birk::fused_fwd_bwd_kernel<4, IO>), grid_for(B), dim3(kBlock), 0, s, logits, dT, T, dual,
+                           dH, B, tol, max_iter);
+    else
+        hipLaunchKernelGGL((birk::fused_fwd_bwd_kernel<8, IO>), grid_for(B), dim3(kBlock), 0, s, logits, dT, T, dual,
+                           dH, B, tol, max_iter);
+    return launched();
+}
+
 }  // namespace
 
 extern "C" {
@@ -129,6 +147,16 @@ int birkhoff_fwd_bf16(const uint16_t* logits, uint16_t* T, float* dual, int64_t 
 int birkhoff_bwd_bf16(const uint16_t* logits, const float* dual, const uint16_t* dT, uint16_t* dH, int64_t B, int n,
                       void* stream) {
     return bwd_entry<uint16_t>(logits, dual, dT, dH, B, n, stream);
+}
+
+int birkhoff_fwd_bwd(const float* logits, const float* dT, float* T, float* dual, float* dH, int64_t B, int n,
+                     float tol, int max_iter, void* stream) {
+    return fused_entry<float>(logits, dT, T, dual, dH, B, n, tol, max_iter, stream);
+}
+
+int birkhoff_fwd_bwd_bf16(const uint16_t* logits, const uint16_t* dT, uint16_t* T, float* dual, uint16_t* dH,
+                          int64_t B, int n, float tol, int max_iter, void* stream) {
+    return fused_entry<uint16_t>(logits, dT, T, dual, dH, B, n, tol, max_iter, stream);
 }
 
 const char* birkhoff_strerror(int code) {

@@ -368,35 +368,35 @@ __device__ __forceinline__ void load_own(const IO* __restrict__ p, int64_t b, fl
 // ---------------------------------------------------------------------------
 // Forward: Newton on the reduced dual (eq 8), one matrix per lane.
 // ---------------------------------------------------------------------------
-template <int N, typename IO, bool kStats>
-__global__ void __launch_bounds__(kBlock)
-newton_fwd_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, float* __restrict__ dual,
-                  int32_t* __restrict__ iters, int64_t B, float tol, int max_iter) {
+
+// Loads the wave's logits, evaluates T at x^(0) = 0 and runs Newton's method to
+// column-sum residual <= tol or max_iter updates.  On return T is the last
+// iterate, y its dual (base-2 units, y_{N-1} = 0 implied), res its residual;
+// returns the number of updates.  The logits are needed again only by the
+// rare fallback sweep, which re-reads this lane's matrix; they do not stay in
+// registers through the loop.
+template <int N, typename IO>
+__device__ __forceinline__ int newton_solve(const Geometry<N, IO>& geo, uint4* lds, const IO* __restrict__ logits,
+                                            float tol, int max_iter, float (&T_out)[N * N], float (&y_out)[N - 1],
+                                            float& res_out) {
     constexpr int M = N - 1;
     using G = Geometry<N, IO>;
-    __shared__ uint4 lds[kWaves][G::Tile::kLdsChunks];
-    const G geo(B);
-    if (geo.nvalid == 0) return;
-    const bool valid = geo.lane < geo.nvalid;
     const int64_t b = geo.base + geo.lane;
-
-    // The logits are needed again only by the rare fallback sweep, which
-    // re-reads them; they do not stay in registers through the loop.
-    float T[N * N], c[N];
-    float y[M];
+    // the iteration works on locals, copied out at the end (keeps the loop in registers)
+    float T[N * N], y[M], c[N], res;
 #pragma unroll
     for (int j = 0; j < M; ++j) y[j] = 0.0f;   // x^(0) = 0
     {
         float L[N * N];
         uint4 w[G::C];
-        G::Tile::load(geo.chunks(logits), geo.nvalid * G::C, lds[geo.wave], geo.lane, w);
+        G::Tile::load(geo.chunks(logits), geo.nvalid * G::C, lds, geo.lane, w);
         Storage<IO>::template decode<N * N>(w, L);
 #pragma unroll
         for (int k = 0; k < N * N; ++k) L[k] *= kLog2e;
         softmax_rows<N>(L, y, T);
     }
     col_sums<N>(T, c);
-    float res = valid ? col_residual<N>(c) : 0.0f;
+    res = geo.lane < geo.nvalid ? col_residual<N>(c) : 0.0f;   // lanes past the end are done
     int it = 0;
 
     while (res > tol && it < max_iter) {
@@ -446,25 +446,95 @@ newton_fwd_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, float* _
         ++it;
         res = col_residual<N>(c);
     }
+#pragma unroll
+    for (int k = 0; k < N * N; ++k) T_out[k] = T[k];
+#pragma unroll
+    for (int j = 0; j < M; ++j) y_out[j] = y[j];
+    res_out = res;
+    return it;
+}
 
+// Writes the wave's T through its LDS tile and, per valid lane, the dual
+// (natural units, beta_{N-1} = 0).
+template <int N, typename IO>
+__device__ __forceinline__ void store_forward(const Geometry<N, IO>& geo, uint4* lds, IO* __restrict__ Tout,
+                                              float* __restrict__ dual, const float (&T)[N * N],
+                                              const float (&y)[N - 1]) {
+    using G = Geometry<N, IO>;
     {
         uint4 w[G::C];
         Storage<IO>::template encode<N * N>(T, w);
-        G::Tile::store(w, lds[geo.wave], geo.lane, geo.chunks(Tout), geo.nvalid * G::C);
+        G::Tile::store(w, lds, geo.lane, geo.chunks(Tout), geo.nvalid * G::C);
     }
-    if (valid) {
+    if (geo.lane < geo.nvalid) {
         float beta[N];
 #pragma unroll
-        for (int j = 0; j < M; ++j) beta[j] = y[j] * kLn2;
-        beta[M] = 0.0f;
-        store_dual<N>(dual, b, beta);
-        if (kStats) iters[b] = (res <= tol) ? it : -1;
+        for (int j = 0; j < N - 1; ++j) beta[j] = y[j] * kLn2;
+        beta[N - 1] = 0.0f;
+        store_dual<N>(dual, geo.base + geo.lane, beta);
     }
 }
 
+template <int N, typename IO, bool kStats>
+__global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(N == 4 ? 7 : 1)))
+newton_fwd_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, float* __restrict__ dual,
+                  int32_t* __restrict__ iters, int64_t B, float tol, int max_iter) {
+    using G = Geometry<N, IO>;
+    __shared__ uint4 lds[kWaves][G::Tile::kLdsChunks];
+    const G geo(B);
+    if (geo.nvalid == 0) return;
+    float T[N * N], y[N - 1], res;
+    const int it = newton_solve<N, IO>(geo, lds[geo.wave], logits, tol, max_iter, T, y, res);
+    store_forward<N, IO>(geo, lds[geo.wave], Tout, dual, T, y);
+    if (kStats && geo.lane < geo.nvalid) iters[geo.base + geo.lane] = (res <= tol) ? it : -1;
+}
+
 // ---------------------------------------------------------------------------
-// Backward: eq (13) at T recomputed from (logits, dual), one matrix per lane.
+// Backward: eq (13), one matrix per lane.
 // ---------------------------------------------------------------------------
+
+// dH = d<G, T>/dH at the projection T, for upstream G = dL/dT.  eq (13) with
+// eta = 1, a = b = 1 and the sign flipped for H = -M ([P] section 4.2):
+//   mu_r = (G o T) 1,  rhs = mu_c - T_{-n}^T mu_r = sum_i T_ij (G_ij - mu_r_i),
+//   Delta = I - T_{-n}^T T_{-n} (the Hessian at the optimum), w_{-n} = Delta^{-1} rhs, w_n = 0,
+//   v = mu_r - T_{-n} w_{-n},  dH = -D = (G - v 1^T - 1 w^T) o T.
+template <int N>
+__device__ __forceinline__ void implicit_grad(const float (&T)[N * N], const float (&G)[N * N], float (&out)[N * N]) {
+    constexpr int M = N - 1;
+    float mur[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        float s = G[i * N] * T[i * N];
+#pragma unroll
+        for (int j = 1; j < N; ++j) s = fmaf(G[i * N + j], T[i * N + j], s);
+        mur[i] = s;
+    }
+    float rhs[M];
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+        float s = T[j] * (G[j] - mur[0]);
+#pragma unroll
+        for (int i = 1; i < N; ++i) s = fmaf(T[i * N + j], G[i * N + j] - mur[i], s);
+        rhs[j] = s;
+    }
+    float h[Tri<N>::S], w[M];
+    hessian<N>(T, h);
+    SpdSolve<N>::run(h, rhs, w);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        float v = mur[i];
+#pragma unroll
+        for (int j = 0; j < M; ++j) v = fmaf(-T[i * N + j], w[j], v);
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            const float wj = (j < M) ? w[j] : 0.0f;
+            out[i * N + j] = (G[i * N + j] - v - wj) * T[i * N + j];
+        }
+    }
+}
+
+// T is recomputed from (logits, dual) as a row softmax ([P] section 4.2: Delta
+// may be recomputed from T* instead of saving the last Hessian).
 template <int N, typename IO>
 __global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(N == 4 ? 8 : 1)))
 implicit_bwd_kernel(const IO* __restrict__ logits, const float* __restrict__ dual, const IO* __restrict__ dT,
@@ -502,42 +572,43 @@ implicit_bwd_kernel(const IO* __restrict__ logits, const float* __restrict__ dua
 #pragma unroll
     for (int j = 0; j < M; ++j) y[j] = (beta[j] - beta[M]) * kLog2e;   // T is invariant to the gauge
     float T[N * N];
-    softmax_rows<N>(L, y, T);   // recompute T* ([P] section 4.2)
-
-    // mu_r = (G o T) 1;  rhs = mu_c - T_{-n}^T mu_r = sum_i T_ij (G_ij - mu_r_i)
-    float mur[N];
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        float s = G[i * N] * T[i * N];
-#pragma unroll
-        for (int j = 1; j < N; ++j) s = fmaf(G[i * N + j], T[i * N + j], s);
-        mur[i] = s;
-    }
-    float rhs[M];
-#pragma unroll
-    for (int j = 0; j < M; ++j) {
-        float s = T[j] * (G[j] - mur[0]);
-#pragma unroll
-        for (int i = 1; i < N; ++i) s = fmaf(T[i * N + j], G[i * N + j] - mur[i], s);
-        rhs[j] = s;
-    }
-    // Delta = I - T_{-n}^T T_{-n} (= the Hessian at the optimum), w_{-n} = Delta^{-1} rhs, w_n = 0
-    float h[Tri<N>::S], w[M];
-    hessian<N>(T, h);
-    SpdSolve<N>::run(h, rhs, w);
-    // v = mu_r - T_{-n} w_{-n};  dH = -D = (G - v 1^T - 1 w^T) o T
+    softmax_rows<N>(L, y, T);
     float out[N * N];
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        float v = mur[i];
-#pragma unroll
-        for (int j = 0; j < M; ++j) v = fmaf(-T[i * N + j], w[j], v);
-#pragma unroll
-        for (int j = 0; j < N; ++j) {
-            const float wj = (j < M) ? w[j] : 0.0f;
-            out[i * N + j] = (G[i * N + j] - v - wj) * T[i * N + j];
-        }
+    implicit_grad<N>(T, G, out);
+    {
+        uint4 wo[C];
+        Storage<IO>::template encode<N * N>(out, wo);
+        Gm::Tile::store(wo, lds[geo.wave], geo.lane, geo.chunks(dH), geo.nvalid * C);
     }
+}
+
+// ---------------------------------------------------------------------------
+// Forward and backward in one launch, for callers that hold dL/dT when they
+// project.  The forward is newton_fwd_kernel's; the backward is eq (13) at the
+// final iterate T, still in registers, so neither the logits nor the dual are
+// read back.  Reads logits and dT, writes T, dual and dH.
+// ---------------------------------------------------------------------------
+template <int N, typename IO>
+__global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(N == 4 ? 7 : 1)))
+fused_fwd_bwd_kernel(const IO* __restrict__ logits, const IO* __restrict__ dT, IO* __restrict__ Tout,
+                     float* __restrict__ dual, IO* __restrict__ dH, int64_t B, float tol, int max_iter) {
+    using Gm = Geometry<N, IO>;
+    constexpr int C = Gm::C;
+    __shared__ uint4 lds[kWaves][Gm::Tile::kLdsChunks];
+    const Gm geo(B);
+    if (geo.nvalid == 0) return;
+    float T[N * N], y[N - 1], res;
+    newton_solve<N, IO>(geo, lds[geo.wave], logits, tol, max_iter, T, y, res);
+    uint4 tg[C];
+    Gm::Tile::fetch(geo.chunks(dT), geo.nvalid * C, geo.lane, tg);   // in flight while T is stored
+    store_forward<N, IO>(geo, lds[geo.wave], Tout, dual, T, y);
+    float G[N * N], out[N * N];
+    {
+        uint4 w[C];
+        Gm::Tile::route(tg, lds[geo.wave], geo.lane, w);
+        Storage<IO>::template decode<N * N>(w, G);
+    }
+    implicit_grad<N>(T, G, out);
     {
         uint4 wo[C];
         Storage<IO>::template encode<N * N>(out, wo);

@@ -136,7 +136,9 @@ def bytes_per_projection(n: int, io: str, passes: str) -> int:
     """Algorithmic HBM bytes per projection: each input read once, each output written once.
 
     fwd: logits + T (n*n elements of the storage type each) + dual (n fp32);
-    bwd: logits + dual + dT + dH.
+    bwd: logits + dual + dT + dH;
+    fused (forward and backward in one launch): logits + dT + T + dual + dH;
+    fwd+bwd: the two separate passes.
     """
     s = 2 if io == "bf16" else 4
     fwd = 2 * n * n * s + 4 * n
@@ -145,4 +147,8 @@ def bytes_per_projection(n: int, io: str, passes: str) -> int:
         return fwd
     if passes == "bwd":
         return bwd
-    return fwd + bwd
+    if passes == "fused":
+        return 4 * n * n * s + 4 * n
+    if passes == "fwd+bwd":
+        return fwd + bwd
+    raise ValueError("unknown passes %r" % (passes,))

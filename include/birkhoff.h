@@ -99,6 +99,22 @@ int birkhoff_fwd_bf16(const uint16_t* logits, uint16_t* T, float* dual, int64_t 
 int birkhoff_bwd_bf16(const uint16_t* logits, const float* dual, const uint16_t* dT,
                       uint16_t* dH, int64_t B, int n, void* stream);
 
+/* Forward and backward in one launch, for callers that already hold dL/dT when
+ * they project (a training step that has the loss gradient at hand, or a fused
+ * benchmark pass).  Computes exactly what birkhoff_fwd computes (T and dual
+ * are bit-identical to it) and then dH by eq (13) at the final iterate T, still
+ * in registers, instead of recomputing T from (logits, dual) as birkhoff_bwd
+ * does; dH therefore agrees with birkhoff_fwd + birkhoff_bwd up to rounding.
+ * Moves 4n^2 s + 4n bytes per matrix (s = storage bytes per element) instead of
+ * the 5n^2 s + 8n of the two separate calls, in one launch.
+ *   logits [B, n, n] input H;  dT [B, n, n] input dL/dT
+ *   T      [B, n, n] output;   dual [B, n] fp32 output;  dH [B, n, n] output dL/dH
+ *   n, tol, max_iter as for birkhoff_fwd.  No argument may alias another. */
+int birkhoff_fwd_bwd(const float* logits, const float* dT, float* T, float* dual, float* dH, int64_t B, int n,
+                     float tol, int max_iter, void* stream);
+int birkhoff_fwd_bwd_bf16(const uint16_t* logits, const uint16_t* dT, uint16_t* T, float* dual, uint16_t* dH,
+                          int64_t B, int n, float tol, int max_iter, void* stream);
+
 /* Static description of a return code (never NULL). */
 const char* birkhoff_strerror(int code);
 

@@ -32,7 +32,8 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_symbols()
     for n in ("birkhoff_fwd", "birkhoff_fwd_ex", "birkhoff_bwd", "sinkhorn_fwd",
-              "birkhoff_fwd_bf16", "birkhoff_bwd_bf16", "birkhoff_strerror", "birkhoff_abi_version"):
+              "birkhoff_fwd_bf16", "birkhoff_bwd_bf16", "birkhoff_fwd_bwd", "birkhoff_fwd_bwd_bf16",
+              "birkhoff_strerror", "birkhoff_abi_version"):
         assert n in names
 
 
@@ -93,6 +94,31 @@ def test_null_and_misaligned_pointers(lib):
         assert lib.birkhoff_bwd(*ptrs, B, n, None) == EALIGN
     assert lib.sinkhorn_fwd(None, P[1], B, n, 20, None) == EINVAL
     assert lib.sinkhorn_fwd(P[0] + 4, P[1], B, n, 20, None) == EALIGN
+
+
+@pytest.mark.parametrize("B,n,tol,it,want", [
+    (-1, 4, 1e-6, 50, EINVAL),
+    (5, 5, 1e-6, 50, EINVAL),
+    (5, 4, 0.0, 50, EINVAL),
+    (5, 4, math.nan, 50, EINVAL),
+    (5, 4, 1e-6, 0, EINVAL),
+    (0, 8, 1e-6, 50, 0),
+])
+def test_fused_argument_checks(lib, B, n, tol, it, want):
+    Q = [A, A + 4096, A + 8192, A + 12288, A + 16384]
+    assert lib.birkhoff_fwd_bwd(*Q, B, n, tol, it, None) == want
+    assert lib.birkhoff_fwd_bwd_bf16(*Q, B, n, tol, it, None) == want
+
+
+def test_fused_null_and_misaligned_pointers(lib):
+    Q = [A, A + 4096, A + 8192, A + 12288, A + 16384]
+    for k in range(5):
+        ptrs = list(Q)
+        ptrs[k] = None
+        assert lib.birkhoff_fwd_bwd(*ptrs, 9, 4, 1e-6, 50, None) == EINVAL
+        ptrs[k] = Q[k] + 8
+        assert lib.birkhoff_fwd_bwd(*ptrs, 9, 4, 1e-6, 50, None) == EALIGN
+        assert lib.birkhoff_fwd_bwd_bf16(*ptrs, 9, 8, 1e-6, 50, None) == EALIGN
 
 
 def test_backward_and_sinkhorn_argument_checks(lib):

@@ -364,3 +364,87 @@ def test_newton_versus_sinkhorn20_on_hard_inputs():
         e_newton.max().item(), e_newton.median().item(), e_sk.max().item(), e_sk.median().item()))
     assert e_newton.max().item() < 1e-4
     assert e_sk.max().item() > 100 * e_newton.max().item()
+
+
+# ------------------------------------------- forward + backward in one launch
+
+def run_fused(w, Hs, Gs):
+    B, n = Hs.shape[0], w.n
+    H = as_storage(Hs, w)
+    G = as_storage(Gs, w)
+    T = torch.empty_like(H)
+    dH = torch.empty_like(G)
+    dual = torch.empty((B, n), dtype=torch.float32, device=DEV)
+    if w.io == "bf16":
+        bp.birkhoff_fwd_bwd_bf16(H, G, T, dual, dH, w.tol, w.max_iter)
+    else:
+        bp.birkhoff_fwd_bwd(H, G, T, dual, dH, w.tol, w.max_iter)
+    return H, G, T, dual, dH
+
+
+@pytest.mark.parametrize("key,B", [("pr1", None), ("train", 8192 + 37), ("n8", 4096 + 19), ("bw", 8192 + 37)])
+def test_fused_parity_and_agreement_with_separate_calls(key, B):
+    """One-launch forward + backward against the oracle; its T and dual are the
+    separate forward's bit for bit, its dH agrees with the separate backward."""
+    w = W.WORKLOADS[key]
+    print("case fused", key, B, flush=True)
+    Hs = W.make_logits(w, B=B)
+    Gs = W.make_upstream(w, B=B)
+    H64 = W.decode_f64(Hs)
+    H, G, T, dual, dH = run_fused(w, Hs, Gs)
+    _, T2, dual2, _ = run_fwd(w, Hs)
+    dH2 = run_bwd(w, H, dual2, Gs)
+    torch.cuda.synchronize()
+    assert torch.equal(T, T2) and torch.equal(dual, dual2)
+    T_ref, _, st = oracle.project(H64, sk_cap=w.sk_cap)
+    assert (st >= 0).all()
+    check_forward(w, H64, host_f64(T), dual.cpu().numpy().astype(np.float64), T_ref)
+    dH_ref = oracle.bwd(T_ref, W.decode_f64(Gs))
+    rel = check_backward(w, host_f64(dH), dH_ref)
+    rel2 = check_backward(w, host_f64(dH2), dH_ref)
+    print("  fused bwd rel %.2e, separate bwd rel %.2e" % (rel, rel2))
+
+
+@pytest.mark.parametrize("key", ["train", "bw"])
+def test_fused_full_size_sampled(key):
+    w = W.WORKLOADS[key]
+    print("case fused full", key, w.B, flush=True)
+    Hs = W.make_logits(w)
+    Gs = W.make_upstream(w)
+    H, G, T, dual, dH = run_fused(w, Hs, Gs)
+    torch.cuda.synchronize()
+    assert torch.isfinite(T.float()).all().item() and torch.isfinite(dH.float()).all().item()
+    idx = sample_indices(w.B)
+    it = torch.from_numpy(idx).to(DEV)
+    H64 = W.decode_f64(Hs[idx])
+    T_ref, _, st = oracle.project(H64, sk_cap=w.sk_cap)
+    assert (st >= 0).all()
+    check_forward(w, H64, host_f64(T[it]), dual[it].cpu().numpy().astype(np.float64), T_ref)
+    check_backward(w, host_f64(dH[it]), oracle.bwd(T_ref, W.decode_f64(Gs[idx])))
+
+
+@pytest.mark.parametrize("B", [1, 63, 64, 65, 257])
+@pytest.mark.parametrize("n", [4, 8])
+def test_fused_ragged_batches_and_canaries(B, n):
+    print("case fused ragged", B, n, flush=True)
+    w = W.WORKLOADS["pr1" if n == 4 else "n8"]
+    Hs = W.make_logits(w, B=B, seed=3000 + B)
+    Gs = W.make_upstream(w, B=B, seed=4000 + B)
+    pad, sentinel = 3, -777.0
+    bufs = [torch.full((B + 2 * pad, n, n), sentinel, device=DEV) for _ in range(2)]
+    Dbuf = torch.full((B + 2 * pad, n), sentinel, device=DEV)
+    T, dH, dual = bufs[0][pad:pad + B], bufs[1][pad:pad + B], Dbuf[pad:pad + B]
+    bp.birkhoff_fwd_bwd(dev(Hs), dev(Gs), T, dual, dH, w.tol, w.max_iter)
+    torch.cuda.synchronize()
+    for buf in bufs + [Dbuf]:
+        assert (buf[:pad] == sentinel).all() and (buf[pad + B:] == sentinel).all()
+    H64 = Hs.astype(np.float64)
+    T_ref, _, _ = oracle.project(H64)
+    check_forward(w, H64, host_f64(T), dual.cpu().numpy().astype(np.float64), T_ref)
+    check_backward(w, host_f64(dH), oracle.bwd(T_ref, Gs.astype(np.float64)))
+
+
+def test_fused_empty_batch_is_a_noop():
+    H = torch.empty((0, 4, 4), device=DEV)
+    T, dual, dH = bp.project_fwd_bwd(H, torch.empty((0, 4, 4), device=DEV))
+    assert T.shape == (0, 4, 4) and dual.shape == (0, 4) and dH.shape == (0, 4, 4)
