@@ -112,6 +112,23 @@ struct Storage<uint16_t> {
     }
 };
 
+// ---- streaming global accesses -------------------------------------------
+//
+// Every byte of a batch is read or written exactly once per launch, so matrix
+// and dual traffic uses non-temporal 16-byte accesses (the caches do not keep
+// lines that will not be touched again).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 stream_load(const uint4* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void stream_store(uint4* p, const uint4& v) {
+    const u32x4_t w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+}
+
 // ---- movement of one matrix per lane between HBM and registers ------------
 //
 // A wave owns 64 consecutive matrices, one per lane, each C 16-byte chunks long
@@ -155,12 +172,12 @@ struct WaveTile {
     __device__ __forceinline__ static void fetch(const uint4* __restrict__ src, int valid, int lane, uint4 (&t)[C]) {
         if (valid == 64 * C) {
 #pragma unroll
-            for (int k = 0; k < C; ++k) t[k] = src[chunk(k, lane)];
+            for (int k = 0; k < C; ++k) t[k] = stream_load(src + chunk(k, lane));
         } else {
 #pragma unroll
             for (int k = 0; k < C; ++k) {
                 const int c = chunk(k, lane);
-                t[k] = src[c < valid ? c : valid - 1];
+                t[k] = stream_load(src + (c < valid ? c : valid - 1));
             }
 #pragma unroll
             for (int k = 0; k < C; ++k) {
@@ -211,26 +228,26 @@ struct WaveTile {
 #pragma unroll
                 for (int k = 0; k < C; ++k) {
                     const int c = chunk(k, lane);
-                    dst[c] = lds[slot(c / C, c % C)];
+                    stream_store(dst + c, lds[slot(c / C, c % C)]);
                 }
             } else {
 #pragma unroll
                 for (int k = 0; k < C; ++k) {
                     const int c = chunk(k, lane);
                     const uint4 v = lds[slot(c / C, c % C)];
-                    if (c < valid) dst[c] = v;
+                    if (c < valid) stream_store(dst + c, v);
                 }
             }
             wave_lds_sync();
         } else {
             if (full) {
 #pragma unroll
-                for (int k = 0; k < C; ++k) dst[chunk(k, lane)] = own[k];
+                for (int k = 0; k < C; ++k) stream_store(dst + chunk(k, lane), own[k]);
             } else {
 #pragma unroll
                 for (int k = 0; k < C; ++k) {
                     const int c = chunk(k, lane);
-                    if (c < valid) dst[c] = own[k];
+                    if (c < valid) stream_store(dst + c, own[k]);
                 }
             }
         }

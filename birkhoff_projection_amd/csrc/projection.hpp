@@ -335,21 +335,23 @@ struct Geometry {
 
 template <int N>
 __device__ __forceinline__ void store_dual(float* __restrict__ dual, int64_t b, const float (&beta)[N]) {
-    float4* q = reinterpret_cast<float4*>(dual + b * N);
+    uint4* q = reinterpret_cast<uint4*>(dual + b * N);
 #pragma unroll
-    for (int k = 0; k < N / 4; ++k) q[k] = make_float4(beta[4 * k], beta[4 * k + 1], beta[4 * k + 2], beta[4 * k + 3]);
+    for (int k = 0; k < N / 4; ++k)
+        stream_store(q + k, make_uint4(__float_as_uint(beta[4 * k]), __float_as_uint(beta[4 * k + 1]),
+                                       __float_as_uint(beta[4 * k + 2]), __float_as_uint(beta[4 * k + 3])));
 }
 
 template <int N>
 __device__ __forceinline__ void load_dual(const float* __restrict__ dual, int64_t b, float (&beta)[N]) {
-    const float4* q = reinterpret_cast<const float4*>(dual + b * N);
+    const uint4* q = reinterpret_cast<const uint4*>(dual + b * N);
 #pragma unroll
     for (int k = 0; k < N / 4; ++k) {
-        const float4 t = q[k];
-        beta[4 * k] = t.x;
-        beta[4 * k + 1] = t.y;
-        beta[4 * k + 2] = t.z;
-        beta[4 * k + 3] = t.w;
+        const uint4 t = stream_load(q + k);
+        beta[4 * k] = __uint_as_float(t.x);
+        beta[4 * k + 1] = __uint_as_float(t.y);
+        beta[4 * k + 2] = __uint_as_float(t.z);
+        beta[4 * k + 3] = __uint_as_float(t.w);
     }
 }
 
@@ -536,7 +538,7 @@ __device__ __forceinline__ void implicit_grad(const float (&T)[N * N], const flo
 // T is recomputed from (logits, dual) as a row softmax ([P] section 4.2: Delta
 // may be recomputed from T* instead of saving the last Hessian).
 template <int N, typename IO>
-__global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(N == 4 ? 8 : 1)))
+__global__ void __launch_bounds__(kBlock)
 implicit_bwd_kernel(const IO* __restrict__ logits, const float* __restrict__ dual, const IO* __restrict__ dT,
                     IO* __restrict__ dH, int64_t B) {
     constexpr int M = N - 1;
