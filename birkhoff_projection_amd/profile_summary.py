@@ -31,7 +31,7 @@ ROOT = pathlib.Path(__file__).resolve().parent.parent
 
 # device kernel -> the C-ABI entry point that launches it
 ENTRY = (("newton_fwd_kernel", "birkhoff_fwd"), ("implicit_bwd_kernel", "birkhoff_bwd"),
-         ("sinkhorn_kernel", "sinkhorn_fwd"), ("fused_kernel", "birkhoff_fwd_bwd"))
+         ("sinkhorn_kernel", "sinkhorn_fwd"), ("fused_fwd_bwd_kernel", "birkhoff_fwd_bwd"))
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -89,45 +89,50 @@ def per_kernel(cnt, counter):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", required=True)
-    ap.add_argument("--stats", required=True)
+    ap.add_argument("--stats", required=True, action="append",
+                    help="a kernel-trace directory; may be repeated (one section each)")
     ap.add_argument("--fetch", required=True)
     ap.add_argument("--write", required=True)
     ap.add_argument("--copy-mib", type=int, required=True)
-    ap.add_argument("--cmd-stats", required=True)
+    ap.add_argument("--cmd-stats", required=True, action="append")
     ap.add_argument("--cmd-fetch", required=True)
     ap.add_argument("--cmd-write", required=True)
     ap.add_argument("--sq")
     ap.add_argument("--cmd-sq")
-    ap.add_argument("--bench-json", help="bench.py JSON line of the run that was traced")
+    ap.add_argument("--bench-json", action="append", default=[],
+                    help="bench.py JSON line of each traced run, in the order of --stats")
     ap.add_argument("--out", default=str(ROOT / "profiles"))
     a = ap.parse_args()
     out = pathlib.Path(a.out)
     out.mkdir(parents=True, exist_ok=True)
     digest = hipbuild.kernel_source_digest()
 
-    st = kernel_stats(a.stats)
+    if len(a.cmd_stats) != len(a.stats):
+        raise SystemExit("give one --cmd-stats per --stats")
     lines = ["# Kernel durations, workload `%s`" % a.workload, "",
-             "Command (run from /tmp with TMPDIR=/tmp; `$R` is the repository root):", "",
-             "    " + a.cmd_stats, "",
              "Kernel sources digest `%s`. Durations are rocprofv3 kernel-trace times per dispatch "
-             "(warm-up launches included)." % digest, "",
-             "| kernel | entry point | calls | avg us | min us | max us | % of GPU time |",
-             "|---|---|---|---|---|---|---|"]
-    for r in st:
-        lines.append("| `%s` | %s | %d | %.2f | %.2f | %.2f | %.1f |" % (
-            r["name"].split("(")[0], entry_of(r["name"]) or "-", r["calls"], r["avg_us"], r["min_us"],
-            r["max_us"], r["pct"]))
-    la = loop_averages(a.stats)
-    lines += ["", "Back-to-back launches of one kernel alone (the longest run of consecutive dispatches "
-              "of each kernel in the trace; bench.py times the same loop with HIP events):", "",
-              "| kernel | entry point | launches | avg us |", "|---|---|---|---|"]
-    for k, (cnt, avg) in sorted(la.items()):
-        lines.append("| `%s` | %s | %d | %.2f |" % (k.split("(")[0], entry_of(k) or "-", cnt, avg))
-    if a.bench_json:
-        b = json.loads(pathlib.Path(a.bench_json).read_text().strip().splitlines()[-1])
-        lines += ["", "bench.py's own HIP-event figures in the same run: %s ms per step; per-kernel average "
-                  "launch %s ms." % (round(b["ms_per_step"], 5),
-                                     {k: round(v, 5) for k, v in b["kernels_ms"].items()})]
+             "(warm-up launches included). Commands run from /tmp with TMPDIR=/tmp; `$R` is the "
+             "repository root." % digest]
+    for k_run, (d, cmd) in enumerate(zip(a.stats, a.cmd_stats)):
+        lines += ["", "## Run %d" % (k_run + 1), "", "    " + cmd, "",
+                  "| kernel | entry point | calls | avg us | min us | max us | % of GPU time |",
+                  "|---|---|---|---|---|---|---|"]
+        for r in kernel_stats(d):
+            lines.append("| `%s` | %s | %d | %.2f | %.2f | %.2f | %.1f |" % (
+                r["name"].split("(")[0], entry_of(r["name"]) or "-", r["calls"], r["avg_us"], r["min_us"],
+                r["max_us"], r["pct"]))
+        la = loop_averages(d)
+        lines += ["", "Back-to-back launches of one kernel alone (the longest run of consecutive dispatches "
+                  "of each kernel; bench.py times the same loops with HIP events):", "",
+                  "| kernel | entry point | launches | avg us |", "|---|---|---|---|"]
+        for k, (cnt, avg) in sorted(la.items()):
+            lines.append("| `%s` | %s | %d | %.2f |" % (k.split("(")[0], entry_of(k) or "-", cnt, avg))
+        if k_run < len(a.bench_json):
+            b = json.loads(pathlib.Path(a.bench_json[k_run]).read_text().strip().splitlines()[-1])
+            lines += ["", "bench.py's own HIP-event figures in the same run (path `%s`): %s ms per step; "
+                      "per-kernel average launch %s ms." % (
+                          b["config"].get("path", "separate"), round(b["ms_per_step"], 5),
+                          {k: round(v, 5) for k, v in b["kernels_ms"].items()})]
     (out / ("kernels_%s.md" % a.workload)).write_text("\n".join(lines) + "\n")
 
     fc, wc = counters(a.fetch), counters(a.write)
