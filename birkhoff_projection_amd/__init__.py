@@ -20,7 +20,7 @@ from typing import Optional
 
 __all__ = [
     "BirkhoffError", "library_path", "load_library",
-    "birkhoff_fwd", "birkhoff_fwd_ex", "birkhoff_bwd", "sinkhorn_fwd",
+    "birkhoff_fwd", "birkhoff_fwd_ex", "birkhoff_bwd", "birkhoff_bwd_from_T", "sinkhorn_fwd",
     "birkhoff_fwd_bf16", "birkhoff_bwd_bf16", "birkhoff_fwd_bwd", "birkhoff_fwd_bwd_bf16",
     "birkhoff_strerror", "birkhoff_abi_version",
     "project", "project_bwd", "project_fwd_bwd", "sinkhorn", "BirkhoffProjection",
@@ -57,6 +57,7 @@ def load_library():
         "birkhoff_fwd": [vp, vp, vp, i64, ci, cf, ci, vp],
         "birkhoff_fwd_ex": [vp, vp, vp, vp, i64, ci, cf, ci, vp],
         "birkhoff_bwd": [vp, vp, vp, vp, i64, ci, vp],
+        "birkhoff_bwd_from_T": [vp, vp, vp, i64, ci, vp],
         "sinkhorn_fwd": [vp, vp, i64, ci, ci, vp],
         "birkhoff_fwd_bf16": [vp, vp, vp, i64, ci, cf, ci, vp],
         "birkhoff_bwd_bf16": [vp, vp, vp, vp, i64, ci, vp],
@@ -180,6 +181,17 @@ def birkhoff_bwd(logits, dual, dT, dH, stream=None) -> None:
     _mats(dH, "dH", torch.float32, B, n)
     dev = _same_device(logits, dual, dT, dH)
     _call("birkhoff_bwd", dev, _p(logits), _p(dual), _p(dT), _p(dH), B, n, _stream_handle(stream, dev))
+
+
+def birkhoff_bwd_from_T(T, dT, dH, stream=None) -> None:
+    """Backward from the projection T itself: dH = dL/dlogits from dT (fp32)."""
+    torch = _torch()
+    _mats(T, "T", torch.float32)
+    B, n = T.shape[0], T.shape[1]
+    _mats(dT, "dT", torch.float32, B, n)
+    _mats(dH, "dH", torch.float32, B, n)
+    dev = _same_device(T, dT, dH)
+    _call("birkhoff_bwd_from_T", dev, _p(T), _p(dT), _p(dH), B, n, _stream_handle(stream, dev))
 
 
 def sinkhorn_fwd(logits, T, iters: int = 20, stream=None) -> None:

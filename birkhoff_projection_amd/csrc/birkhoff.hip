@@ -149,6 +149,19 @@ int birkhoff_bwd_bf16(const uint16_t* logits, const float* dual, const uint16_t*
     return bwd_entry<uint16_t>(logits, dual, dT, dH, B, n, stream);
 }
 
+int birkhoff_bwd_from_T(const float* T, const float* dT, float* dH, int64_t B, int n, void* stream) {
+    int rc = check_batch(B, n);
+    if (rc != BIRKHOFF_OK || B == 0) return rc;
+    rc = check_ptrs({T, dT, dH});
+    if (rc != BIRKHOFF_OK) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (n == 4)
+        hipLaunchKernelGGL((birk::implicit_bwd_from_T_kernel<4>), grid_for(B), dim3(kBlock), 0, s, T, dT, dH, B);
+    else
+        hipLaunchKernelGGL((birk::implicit_bwd_from_T_kernel<8>), grid_for(B), dim3(kBlock), 0, s, T, dT, dH, B);
+    return launched();
+}
+
 int birkhoff_fwd_bwd(const float* logits, const float* dT, float* T, float* dual, float* dH, int64_t B, int n,
                      float tol, int max_iter, void* stream) {
     return fused_entry<float>(logits, dT, T, dual, dH, B, n, tol, max_iter, stream);

@@ -60,6 +60,26 @@ __device__ __forceinline__ void softmax_rows(const float (&L)[N * N], const floa
     }
 }
 
+// softmax_rows at beta = 0 (the starting point x^(0) = 0)
+template <int N>
+__device__ __forceinline__ void softmax_rows0(const float (&L)[N * N], float (&T)[N * N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        float mu = L[i * N];
+#pragma unroll
+        for (int j = 1; j < N; ++j) mu = fmaxf(mu, L[i * N + j]);
+        float u[N];
+#pragma unroll
+        for (int j = 0; j < N; ++j) u[j] = ex2(L[i * N + j] - mu);
+        float s = u[0];
+#pragma unroll
+        for (int j = 1; j < N; ++j) s += u[j];
+        const float r = rcp(s);
+#pragma unroll
+        for (int j = 0; j < N; ++j) T[i * N + j] = u[j] * r;
+    }
+}
+
 // column sums c_j = sum_i T_ij (eq 11); the gradient of the reduced dual is c_{-n} - 1 (eq 9)
 template <int N>
 __device__ __forceinline__ void col_sums(const float (&T)[N * N], float (&c)[N]) {
@@ -121,6 +141,24 @@ __device__ __forceinline__ void hessian(const float (&T)[N * N], float (&h)[Tri<
     }
 #pragma unroll
     for (int j = 0; j < M; ++j) h[Tri<N>::at(j, j)] = dg[j];
+}
+
+// Adds 2^-22 tr(H) to the diagonal of the Newton system.  When some column of
+// T is carried by a single entry near 1 (large-magnitude logits), the Hessian
+// has an eigenvalue far below fp32 resolution (1e-8 relative, against a
+// rounding level of 6e-8 in the gradient); the exact inverse then turns that
+// rounding noise into a step of order one along the unresolvable direction,
+// and the line search crawls.  The shift is below the rounding level of every
+// entry of H, so resolvable directions keep their Newton step to within
+// 2^-22 tr(H) / lambda relative, and the fixed point (g = 0) is unchanged.
+template <int N>
+__device__ __forceinline__ void damp(float (&h)[Tri<N>::S]) {
+    float tr = h[Tri<N>::at(0, 0)];
+#pragma unroll
+    for (int j = 1; j < N - 1; ++j) tr += h[Tri<N>::at(j, j)];
+    const float delta = tr * 0x1.0p-22f;
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j) h[Tri<N>::at(j, j)] += delta;
 }
 
 // x = H^{-1} r for the symmetric positive definite (N-1) x (N-1) matrix H.
@@ -219,13 +257,13 @@ __device__ __forceinline__ float trial_point(const float (&T)[N * N], const floa
         em[j] = expm1_from(s[j], e[j]);
         if (j > 0) ssum += s[j];
     }
-    float q = 0.0f;   // prod_i (1 + a_i) - 1
+    float q;   // prod_i (1 + a_i) - 1
 #pragma unroll
     for (int i = 0; i < N; ++i) {
         float t = T[i * N] * em[0];
 #pragma unroll
         for (int j = 1; j < M; ++j) t = fmaf(T[i * N + j], em[j], t);
-        q = fmaf(q, t, q + t);
+        q = (i == 0) ? t : fmaf(q, t, q + t);
     }
     float lsum = 0.0f;   // sum_i log2(rs_i), used when the step is not small
 #pragma unroll
@@ -395,7 +433,7 @@ __device__ __forceinline__ int newton_solve(const Geometry<N, IO>& geo, uint4* l
         Storage<IO>::template decode<N * N>(w, L);
 #pragma unroll
         for (int k = 0; k < N * N; ++k) L[k] *= kLog2e;
-        softmax_rows<N>(L, y, T);
+        softmax_rows0<N>(L, T);
     }
     col_sums<N>(T, c);
     res = geo.lane < geo.nvalid ? col_residual<N>(c) : 0.0f;   // lanes past the end are done
@@ -412,6 +450,7 @@ __device__ __forceinline__ int newton_solve(const Geometry<N, IO>& geo, uint4* l
         }
         float h[Tri<N>::S];
         hessian<N>(T, h);
+        damp<N>(h);
         const bool ok = SpdSolve<N>::run(h, r, d);   // d = -H^{-1} g
 
         bool accepted = false;
@@ -422,9 +461,9 @@ __device__ __forceinline__ int newton_solve(const Geometry<N, IO>& geo, uint4* l
 #pragma unroll
                 for (int j = 0; j < M; ++j) s[j] = gam * d[j];
                 const float df = trial_point<N>(T, s, e, rr, ct);
-                float gt2 = 0.0f;
+                float gt2 = (ct[0] - 1.0f) * (ct[0] - 1.0f);
 #pragma unroll
-                for (int j = 0; j < M; ++j) gt2 = fmaf(ct[j] - 1.0f, ct[j] - 1.0f, gt2);
+                for (int j = 1; j < M; ++j) gt2 = fmaf(ct[j] - 1.0f, ct[j] - 1.0f, gt2);
                 if (df < 0.0f && gt2 < gn2) {
 #pragma unroll
                     for (int j = 0; j < M; ++j) y[j] = fmaf(s[j], kLog2e, y[j]);
@@ -580,6 +619,36 @@ implicit_bwd_kernel(const IO* __restrict__ logits, const float* __restrict__ dua
     {
         uint4 wo[C];
         Storage<IO>::template encode<N * N>(out, wo);
+        Gm::Tile::store(wo, lds[geo.wave], geo.lane, geo.chunks(dH), geo.nvalid * C);
+    }
+}
+
+// The backward from the projection itself ([P] section 4.2: dH needs only T*
+// and G): reads T and dT, writes dH; no exponentials.
+template <int N>
+__global__ void __launch_bounds__(kBlock)
+implicit_bwd_from_T_kernel(const float* __restrict__ Tin, const float* __restrict__ dT, float* __restrict__ dH,
+                           int64_t B) {
+    using Gm = Geometry<N, float>;
+    constexpr int C = Gm::C;
+    __shared__ uint4 lds[kWaves][Gm::Tile::kLdsChunks];
+    const Gm geo(B);
+    if (geo.nvalid == 0) return;
+    uint4 tt[C], tg[C];
+    Gm::Tile::fetch(geo.chunks(Tin), geo.nvalid * C, geo.lane, tt);
+    Gm::Tile::fetch(geo.chunks(dT), geo.nvalid * C, geo.lane, tg);
+    float T[N * N], G[N * N], out[N * N];
+    {
+        uint4 w[C];
+        Gm::Tile::route(tt, lds[geo.wave], geo.lane, w);
+        Storage<float>::template decode<N * N>(w, T);
+        Gm::Tile::route(tg, lds[geo.wave], geo.lane, w);
+        Storage<float>::template decode<N * N>(w, G);
+    }
+    implicit_grad<N>(T, G, out);
+    {
+        uint4 wo[C];
+        Storage<float>::template encode<N * N>(out, wo);
         Gm::Tile::store(wo, lds[geo.wave], geo.lane, geo.chunks(dH), geo.nvalid * C);
     }
 }

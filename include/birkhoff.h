@@ -83,6 +83,16 @@ int birkhoff_fwd_ex(const float* logits, float* T, float* dual, int32_t* iters,
 int birkhoff_bwd(const float* logits, const float* dual, const float* dT, float* dH,
                  int64_t B, int n, void* stream);
 
+/* Backward pass from the projection itself, fp32 storage (section 4.2: the
+ * gradient needs only T* and the upstream G; no dual, no exponentials).
+ *   T  [B, n, n] fp32, a doubly stochastic projection (e.g. birkhoff_fwd's T)
+ *   dT [B, n, n] fp32, upstream gradient dL/dT
+ *   dH [B, n, n] fp32, output dL/dH
+ * Moves 3n^2 * 4 bytes per matrix instead of birkhoff_bwd's 3n^2 * 4 + 4n.
+ * dH agrees with birkhoff_bwd up to rounding (birkhoff_bwd recomputes T from
+ * the logits and the dual; this entry point takes T as given). */
+int birkhoff_bwd_from_T(const float* T, const float* dT, float* dH, int64_t B, int n, void* stream);
+
 /* Comparison baseline: exactly `iters` Sinkhorn-Knopp sweeps (section 2.2 eq (2),
  * evaluated in the log domain as the block coordinate ascent of eq (7)) from
  * v = 1, then T = diag(u) exp(H) diag(v).  One sweep = row then column

@@ -33,6 +33,7 @@ def test_header_declares_the_entry_points():
     names = declared_symbols()
     for n in ("birkhoff_fwd", "birkhoff_fwd_ex", "birkhoff_bwd", "sinkhorn_fwd",
               "birkhoff_fwd_bf16", "birkhoff_bwd_bf16", "birkhoff_fwd_bwd", "birkhoff_fwd_bwd_bf16",
+              "birkhoff_bwd_from_T",
               "birkhoff_strerror", "birkhoff_abi_version"):
         assert n in names
 
@@ -119,6 +120,18 @@ def test_fused_null_and_misaligned_pointers(lib):
         ptrs[k] = Q[k] + 8
         assert lib.birkhoff_fwd_bwd(*ptrs, 9, 4, 1e-6, 50, None) == EALIGN
         assert lib.birkhoff_fwd_bwd_bf16(*ptrs, 9, 8, 1e-6, 50, None) == EALIGN
+
+
+def test_bwd_from_T_argument_checks(lib):
+    assert lib.birkhoff_bwd_from_T(P[0], P[1], P[2], -1, 4, None) == EINVAL
+    assert lib.birkhoff_bwd_from_T(P[0], P[1], P[2], 5, 6, None) == EINVAL
+    assert lib.birkhoff_bwd_from_T(None, None, None, 0, 4, None) == 0
+    for k in range(3):
+        ptrs = list(P[:3])
+        ptrs[k] = None
+        assert lib.birkhoff_bwd_from_T(*ptrs, 5, 8, None) == EINVAL
+        ptrs[k] = P[k] + 4
+        assert lib.birkhoff_bwd_from_T(*ptrs, 5, 8, None) == EALIGN
 
 
 def test_backward_and_sinkhorn_argument_checks(lib):
