@@ -215,6 +215,37 @@ struct WaveTile {
         route(t, lds, lane, own);
     }
 
+    // Asynchronous variant of fetch + route for a staged tile whose contents
+    // are needed much later: the wave's span is copied from global memory
+    // straight into its LDS region (global_load_lds_dwordx4: lane i of access k
+    // writes chunk k*64 + i at byte 16*(k*64 + i) of the region, unswizzled),
+    // holding no registers while it is in flight.  Chunks at or beyond `valid`
+    // repeat the last valid chunk.  The region must not be touched until
+    // read_prefetched.
+    __device__ __forceinline__ static void prefetch(const uint4* __restrict__ src, int valid, uint4* lds, int lane) {
+        static_assert(kStaged, "only staged tiles are prefetched through LDS");
+        typedef __attribute__((address_space(3))) uint4 lds_u4;
+        typedef __attribute__((address_space(3))) void lds_void;
+        lds_u4* base = reinterpret_cast<lds_u4*>(
+            __builtin_amdgcn_readfirstlane(static_cast<int>(reinterpret_cast<uintptr_t>(lds))));
+        wave_lds_sync();   // earlier reads of the region are complete
+#pragma unroll
+        for (int k = 0; k < C; ++k) {
+            const int c = k * 64 + lane;
+            __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + (c < valid ? c : valid - 1)),
+                                             reinterpret_cast<lds_void*>(base + k * 64), 16, 0, 0);
+        }
+    }
+
+    // Waits for a prefetch and hands each lane its own C chunks.
+    __device__ __forceinline__ static void read_prefetched(uint4* lds, int lane, uint4 (&own)[C]) {
+        __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0): the LDS copies have landed
+        wave_lds_sync();
+#pragma unroll
+        for (int q = 0; q < C; ++q) own[q] = lds[lane * C + q];
+        wave_lds_sync();
+    }
+
     // Registers of the owning lane -> global.  `valid` (wave-uniform) chunks
     // exist; the rest are not written.  A full tile stores unconditionally.
     __device__ __forceinline__ static void store(const uint4 (&own)[C], uint4* lds, int lane, uint4* __restrict__ dst,

@@ -415,10 +415,10 @@ __device__ __forceinline__ void load_own(const IO* __restrict__ p, int64_t b, fl
 // returns the number of updates.  The logits are needed again only by the
 // rare fallback sweep, which re-reads this lane's matrix; they do not stay in
 // registers through the loop.
-template <int N, typename IO>
+template <int N, typename IO, bool kPrefetch = false>
 __device__ __forceinline__ int newton_solve(const Geometry<N, IO>& geo, uint4* lds, const IO* __restrict__ logits,
                                             float tol, int max_iter, float (&T_out)[N * N], float (&y_out)[N - 1],
-                                            float& res_out) {
+                                            float& res_out, const IO* __restrict__ prefetch_src = nullptr) {
     constexpr int M = N - 1;
     using G = Geometry<N, IO>;
     const int64_t b = geo.base + geo.lane;
@@ -435,6 +435,9 @@ __device__ __forceinline__ int newton_solve(const Geometry<N, IO>& geo, uint4* l
         for (int k = 0; k < N * N; ++k) L[k] *= kLog2e;
         softmax_rows0<N>(L, T);
     }
+    // optionally start copying another tile of the wave (dL/dT) into the now
+    // free LDS region, to be read after the iteration
+    if constexpr (kPrefetch) G::Tile::prefetch(geo.chunks(prefetch_src), geo.nvalid * G::C, lds, geo.lane);
     col_sums<N>(T, c);
     res = geo.lane < geo.nvalid ? col_residual<N>(c) : 0.0f;   // lanes past the end are done
     int it = 0;
@@ -660,7 +663,7 @@ implicit_bwd_from_T_kernel(const float* __restrict__ Tin, const float* __restric
 // read back.  Reads logits and dT, writes T, dual and dH.
 // ---------------------------------------------------------------------------
 template <int N, typename IO>
-__global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(N == 4 ? 7 : 1)))
+__global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(N == 4 ? 6 : 1)))
 fused_fwd_bwd_kernel(const IO* __restrict__ logits, const IO* __restrict__ dT, IO* __restrict__ Tout,
                      float* __restrict__ dual, IO* __restrict__ dH, int64_t B, float tol, int max_iter) {
     using Gm = Geometry<N, IO>;
@@ -669,12 +672,19 @@ fused_fwd_bwd_kernel(const IO* __restrict__ logits, const IO* __restrict__ dT, I
     const Gm geo(B);
     if (geo.nvalid == 0) return;
     float T[N * N], y[N - 1], res;
-    newton_solve<N, IO>(geo, lds[geo.wave], logits, tol, max_iter, T, y, res);
-    uint4 tg[C];
-    Gm::Tile::fetch(geo.chunks(dT), geo.nvalid * C, geo.lane, tg);   // in flight while T is stored
-    store_forward<N, IO>(geo, lds[geo.wave], Tout, dual, T, y);
     float G[N * N], out[N * N];
-    {
+    if constexpr (Gm::Tile::kStaged) {
+        // dL/dT travels into LDS while the Newton iteration runs
+        newton_solve<N, IO, true>(geo, lds[geo.wave], logits, tol, max_iter, T, y, res, dT);
+        uint4 w[C];
+        Gm::Tile::read_prefetched(lds[geo.wave], geo.lane, w);
+        Storage<IO>::template decode<N * N>(w, G);
+        store_forward<N, IO>(geo, lds[geo.wave], Tout, dual, T, y);
+    } else {
+        newton_solve<N, IO>(geo, lds[geo.wave], logits, tol, max_iter, T, y, res);
+        uint4 tg[C];
+        Gm::Tile::fetch(geo.chunks(dT), geo.nvalid * C, geo.lane, tg);   // in flight while T is stored
+        store_forward<N, IO>(geo, lds[geo.wave], Tout, dual, T, y);
         uint4 w[C];
         Gm::Tile::route(tg, lds[geo.wave], geo.lane, w);
         Storage<IO>::template decode<N * N>(w, G);
