@@ -57,9 +57,11 @@ def kernel_stats(d):
              "pct": float(r["Percentage"])} for r in rows]
 
 
-def loop_averages(d):
+def loop_averages(d, last=0):
     """Average duration (us) of each kernel over its longest run of consecutive
-    dispatches -- the back-to-back launches bench.py times with events."""
+    dispatches -- the back-to-back launches bench.py times with events -- or
+    over the final `last` dispatches of that run (the timed ones, when the run
+    also holds the warm-up launches)."""
     rows = list(csv.DictReader(open(one_csv(d, "_kernel_trace.csv"))))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     best = {}
@@ -72,6 +74,8 @@ def loop_averages(d):
             run_name, run = name, []
         if r:
             run.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    if last > 0:
+        best = {k: v[-last:] for k, v in best.items()}
     return {k: (len(v), sum(v) / len(v)) for k, v in best.items()}
 
 
@@ -102,6 +106,9 @@ def main():
     ap.add_argument("--cmd-sq")
     ap.add_argument("--bench-json", action="append", default=[],
                     help="bench.py JSON line of each traced run, in the order of --stats")
+    ap.add_argument("--timed", type=int, default=0,
+                    help="bench.py --steps of the traced runs: average only the last this many launches "
+                         "of each back-to-back run")
     ap.add_argument("--out", default=str(ROOT / "profiles"))
     a = ap.parse_args()
     out = pathlib.Path(a.out)
@@ -122,9 +129,10 @@ def main():
             lines.append("| `%s` | %s | %d | %.2f | %.2f | %.2f | %.1f |" % (
                 r["name"].split("(")[0], entry_of(r["name"]) or "-", r["calls"], r["avg_us"], r["min_us"],
                 r["max_us"], r["pct"]))
-        la = loop_averages(d)
+        la = loop_averages(d, a.timed)
         lines += ["", "Back-to-back launches of one kernel alone (the longest run of consecutive dispatches "
-                  "of each kernel; bench.py times the same loops with HIP events):", "",
+                  "of each kernel%s; bench.py times the same loops with HIP events):" % (
+                      ", its last %d launches" % a.timed if a.timed else ""), "",
                   "| kernel | entry point | launches | avg us |", "|---|---|---|---|"]
         for k, (cnt, avg) in sorted(la.items()):
             lines.append("| `%s` | %s | %d | %.2f |" % (k.split("(")[0], entry_of(k) or "-", cnt, avg))
