@@ -17,8 +17,12 @@ namespace {
 
 using birk::kBlock;
 
-// Largest batch one launch covers: grid.x <= 2^31 - 1 workgroups of kBlock lanes.
-constexpr int64_t kMaxBatch = (int64_t)0x7fffffff * kBlock;
+// Largest batch one launch covers: grid.x <= 2^31 - 1 workgroups of kBlock lanes,
+// and an 8 x 8 matrix takes two lanes.
+constexpr int64_t kMaxBatch = (int64_t)0x7fffffff * kBlock / 2;
+
+// lanes per matrix, as in the kernels
+int lanes_per_matrix(int n) { return n == 8 ? birk::Split<8>::R : birk::Split<4>::R; }
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
@@ -43,16 +47,19 @@ int check_tol(float tol, int max_iter) {
 
 int launched() { return hipGetLastError() == hipSuccess ? BIRKHOFF_OK : BIRKHOFF_ELAUNCH; }
 
-dim3 grid_for(int64_t B) { return dim3((unsigned)((B + kBlock - 1) / kBlock)); }
+dim3 grid_for(int64_t B, int n) {
+    const int64_t lanes = B * lanes_per_matrix(n);
+    return dim3((unsigned)((lanes + kBlock - 1) / kBlock));
+}
 
 template <int N, typename IO>
 int fwd_launch(const IO* logits, IO* T, float* dual, int32_t* iters, int64_t B, float tol, int max_iter,
                hipStream_t s) {
     if (iters)
-        hipLaunchKernelGGL((birk::newton_fwd_kernel<N, IO, true>), grid_for(B), dim3(kBlock), 0, s, logits, T,
+        hipLaunchKernelGGL((birk::newton_fwd_kernel<N, IO, true>), grid_for(B, N), dim3(kBlock), 0, s, logits, T,
                            dual, iters, B, tol, max_iter);
     else
-        hipLaunchKernelGGL((birk::newton_fwd_kernel<N, IO, false>), grid_for(B), dim3(kBlock), 0, s, logits, T,
+        hipLaunchKernelGGL((birk::newton_fwd_kernel<N, IO, false>), grid_for(B, N), dim3(kBlock), 0, s, logits, T,
                            dual, iters, B, tol, max_iter);
     return launched();
 }
@@ -80,10 +87,10 @@ int bwd_entry(const IO* logits, const float* dual, const IO* dT, IO* dH, int64_t
     if (rc != BIRKHOFF_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (n == 4)
-        hipLaunchKernelGGL((birk::implicit_bwd_kernel<4, IO>), grid_for(B), dim3(kBlock), 0, s, logits, dual, dT, dH,
+        hipLaunchKernelGGL((birk::implicit_bwd_kernel<4, IO>), grid_for(B, 4), dim3(kBlock), 0, s, logits, dual, dT, dH,
                            B);
     else
-        hipLaunchKernelGGL((birk::implicit_bwd_kernel<8, IO>), grid_for(B), dim3(kBlock), 0, s, logits, dual, dT, dH,
+        hipLaunchKernelGGL((birk::implicit_bwd_kernel<8, IO>), grid_for(B, 8), dim3(kBlock), 0, s, logits, dual, dT, dH,
                            B);
     return launched();
 }
@@ -98,10 +105,10 @@ int fused_entry(const IO* logits, const IO* dT, IO* T, float* dual, IO* dH, int6
     if (rc != BIRKHOFF_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (n == 4)
-        hipLaunchKernelGGL((birk::fused_fwd_bwd_kernel<4, IO>), grid_for(B), dim3(kBlock), 0, s, logits, dT, T, dual,
+        hipLaunchKernelGGL((birk::fused_fwd_bwd_kernel<4, IO>), grid_for(B, 4), dim3(kBlock), 0, s, logits, dT, T, dual,
                            dH, B, tol, max_iter);
     else
-        hipLaunchKernelGGL((birk::fused_fwd_bwd_kernel<8, IO>), grid_for(B), dim3(kBlock), 0, s, logits, dT, T, dual,
+        hipLaunchKernelGGL((birk::fused_fwd_bwd_kernel<8, IO>), grid_for(B, 8), dim3(kBlock), 0, s, logits, dT, T, dual,
                            dH, B, tol, max_iter);
     return launched();
 }
@@ -133,9 +140,9 @@ int sinkhorn_fwd(const float* logits, float* T, int64_t B, int n, int iters, voi
     if (rc != BIRKHOFF_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (n == 4)
-        hipLaunchKernelGGL((birk::sinkhorn_kernel<4, float>), grid_for(B), dim3(kBlock), 0, s, logits, T, B, iters);
+        hipLaunchKernelGGL((birk::sinkhorn_kernel<4, float>), grid_for(B, 4), dim3(kBlock), 0, s, logits, T, B, iters);
     else
-        hipLaunchKernelGGL((birk::sinkhorn_kernel<8, float>), grid_for(B), dim3(kBlock), 0, s, logits, T, B, iters);
+        hipLaunchKernelGGL((birk::sinkhorn_kernel<8, float>), grid_for(B, 8), dim3(kBlock), 0, s, logits, T, B, iters);
     return launched();
 }
 
@@ -156,9 +163,9 @@ int birkhoff_bwd_from_T(const float* T, const float* dT, float* dH, int64_t B, i
     if (rc != BIRKHOFF_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (n == 4)
-        hipLaunchKernelGGL((birk::implicit_bwd_from_T_kernel<4>), grid_for(B), dim3(kBlock), 0, s, T, dT, dH, B);
+        hipLaunchKernelGGL((birk::implicit_bwd_from_T_kernel<4>), grid_for(B, 4), dim3(kBlock), 0, s, T, dT, dH, B);
     else
-        hipLaunchKernelGGL((birk::implicit_bwd_from_T_kernel<8>), grid_for(B), dim3(kBlock), 0, s, T, dT, dH, B);
+        hipLaunchKernelGGL((birk::implicit_bwd_from_T_kernel<8>), grid_for(B, 8), dim3(kBlock), 0, s, T, dT, dH, B);
     return launched();
 }
 

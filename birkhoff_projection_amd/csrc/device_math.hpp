@@ -134,21 +134,18 @@ __device__ __forceinline__ void stream_store(uint4* p, const uint4& v) {
 // A wave owns 64 consecutive matrices, one per lane, each C 16-byte chunks long
 // and stored back to back.
 //
-// Small matrices (C <= 4, at most 64 bytes): loading them lane by lane would
-// make every load instruction touch 64 scattered 16-byte pieces of a
-// 64*C*16-byte span, only a quarter of each 64-byte line.  Instead the wave
-// reads (and writes) the span with fully coalesced 16-byte accesses -- chunk
+// Items of up to 128 bytes (C <= 8): loading them lane by lane would make
+// every load instruction touch 64 scattered 16-byte pieces of a
+// 64*C*16-byte span (64 distinct cache lines per instruction, each visited
+// C times), which starves the address path.  Instead the wave reads (and
+// writes) the span with fully coalesced 16-byte accesses -- chunk
 // c = k*64 + lane in instruction k -- and swaps the chunks into their owners'
-// registers through a private region of LDS.  Within a matrix, chunk q sits at
+// registers through a private region of LDS.  Within an item, chunk q sits at
 // slot q ^ f(m), f(m) = (m / (16/C)) mod C, so that the 16 lanes of any LDS
 // access phase hit 16 different 16-byte bank groups on both sides.  Only the
 // issuing wave touches its region, so ordering inside the wave needs no
-// workgroup barrier.
-//
-// Larger matrices (C >= 8, whole 128-byte lines per lane) are read and written
-// by their owners directly: every line an instruction touches is consumed in
-// full by the same lane within the next instructions, and the LDS round trip
-// would cost more registers than it saves.
+// workgroup barrier.  (Larger items would be read and written by their owners
+// directly; none of the kernels has them.)
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -158,7 +155,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 template <int C>
 struct WaveTile {
     static_assert(C == 2 || C == 4 || C == 8 || C == 16, "chunks per matrix");
-    static constexpr bool kStaged = C <= 4;
+    static constexpr bool kStaged = C <= 8;
     static constexpr int kLdsChunks = kStaged ? 64 * C : 1;   // LDS tile per wave, in 16-byte chunks
     __device__ __forceinline__ static int slot(int m, int q) { return m * C + (q ^ ((m / (16 / C)) & (C - 1))); }
     // chunk that a lane handles in access k: coalesced order when staged, its own chunk k otherwise

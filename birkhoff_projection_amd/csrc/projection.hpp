@@ -1,15 +1,22 @@
-// projection.hpp -- per-lane device routines for the batched KL projection
-// onto the Birkhoff polytope and its implicit backward pass (gfx950).
+// projection.hpp -- device routines for the batched KL projection onto the
+// Birkhoff polytope and its implicit backward pass (gfx950).
 //
-// Layout.  One matrix per lane: a wave of 64 lanes owns 64 consecutive
-// matrices, each held entirely in VGPRs (n = 4: 16 entries of T and the
-// 6-entry Hessian triangle).  All arithmetic is per lane -- no cross-lane
-// reductions and no MFMA: the work is tiny and independent per matrix, and the
-// per-matrix scalar logic (the 3x3 solve, the step-size search) runs once per
-// matrix rather than being replicated across a group of lanes.  LDS is used
-// only to turn the matrix loads and stores into coalesced wave-wide accesses
-// (WaveTile).  Control flow is per lane; the wave keeps stepping while any of
-// its lanes is unconverged.
+// Layout.  Each n x n matrix is held entirely in VGPRs by R adjacent lanes,
+// each lane owning K = n / R of its rows: R = 1 for n = 4 (one matrix per
+// lane, 64 per wave; 16 entries of T and the 6-entry Hessian triangle per
+// lane) and R = 2 for n = 8 (a lane pair per matrix, 32 per wave, so that a
+// lane's share of T, the 28-entry Hessian and its Cholesky factor leave room
+// for four or more waves per SIMD).  Row-local work (softmaxes, row sums,
+// trial-point updates) stays in the owning lane; column sums and the Hessian's
+// dot products are completed with one DPP exchange inside the pair.  Both
+// lanes of a pair then hold bit-identical copies of every per-matrix quantity
+// (the exchange adds the two halves in either order, which is the same sum),
+// so the Newton solve and the step-size search run redundantly in both and
+// take identical decisions.  There is no MFMA: the work is tiny and
+// independent per matrix.  LDS is used only to make matrix loads and stores
+// coalesced wave-wide accesses (WaveTile) and, in the fused kernel, to land
+// dL/dT while the iteration runs.  Control flow is per lane (per pair); the
+// wave keeps stepping while any of its matrices is unconverged.
 //
 // Units.  Logits are scaled by log2(e) on load and the dual is kept in the
 // same base-2 units (y = beta * log2 e), so that every exponential is one
@@ -27,6 +34,39 @@ namespace birk {
 
 constexpr int kBlock = 256;  // threads per workgroup (4 waves of 64)
 
+// lanes per matrix
+template <int N>
+struct Split {
+    static constexpr int R = N == 8 ? 2 : 1;
+    static constexpr int K = N / R;   // rows per lane
+};
+
+// Completing a per-matrix sum / maximum / product over the R lanes of a matrix.
+template <int R>
+struct Pair;
+
+template <>
+struct Pair<1> {
+    __device__ __forceinline__ static float sum(float v) { return v; }
+    __device__ __forceinline__ static float max(float v) { return v; }
+    __device__ __forceinline__ static float prod_m1(float q) { return q; }
+};
+
+template <>
+struct Pair<2> {
+    // the partner lane's value: DPP quad_perm [1,0,3,2] swaps lanes 2k and 2k+1
+    __device__ __forceinline__ static float other(float v) {
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+    }
+    __device__ __forceinline__ static float sum(float v) { return v + other(v); }
+    __device__ __forceinline__ static float max(float v) { return fmaxf(v, other(v)); }
+    // (1 + q)(1 + q') - 1 for the two halves' partial products
+    __device__ __forceinline__ static float prod_m1(float q) {
+        const float o = other(q);
+        return fmaf(q, o, q + o);
+    }
+};
+
 // packed lower triangle of an (N-1) x (N-1) symmetric matrix
 template <int N>
 struct Tri {
@@ -37,11 +77,11 @@ struct Tri {
 
 // Rows of T are Softmax(H_i. + beta) ([P] section 3.1), evaluated with the row
 // maximum subtracted as in eq (10):  T_ij = 2^{L_ij + y_j - mu_i} / sum_k 2^{L_ik + y_k - mu_i},
-// with y_{N-1} = 0.  Each row then sums to one up to rounding.
-template <int N>
-__device__ __forceinline__ void softmax_rows(const float (&L)[N * N], const float (&y)[N - 1], float (&T)[N * N]) {
+// with y_{N-1} = 0.  Each row then sums to one up to rounding.  K rows.
+template <int N, int K>
+__device__ __forceinline__ void softmax_rows(const float (&L)[K * N], const float (&y)[N - 1], float (&T)[K * N]) {
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
+    for (int i = 0; i < K; ++i) {
         float u[N];
 #pragma unroll
         for (int j = 0; j < N - 1; ++j) u[j] = L[i * N + j] + y[j];
@@ -61,10 +101,10 @@ __device__ __forceinline__ void softmax_rows(const float (&L)[N * N], const floa
 }
 
 // softmax_rows at beta = 0 (the starting point x^(0) = 0)
-template <int N>
-__device__ __forceinline__ void softmax_rows0(const float (&L)[N * N], float (&T)[N * N]) {
+template <int N, int K>
+__device__ __forceinline__ void softmax_rows0(const float (&L)[K * N], float (&T)[K * N]) {
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
+    for (int i = 0; i < K; ++i) {
         float mu = L[i * N];
 #pragma unroll
         for (int j = 1; j < N; ++j) mu = fmaxf(mu, L[i * N + j]);
@@ -82,13 +122,14 @@ __device__ __forceinline__ void softmax_rows0(const float (&L)[N * N], float (&T
 
 // column sums c_j = sum_i T_ij (eq 11); the gradient of the reduced dual is c_{-n} - 1 (eq 9)
 template <int N>
-__device__ __forceinline__ void col_sums(const float (&T)[N * N], float (&c)[N]) {
+__device__ __forceinline__ void col_sums(const float (&T)[Split<N>::K * N], float (&c)[N]) {
+    constexpr int K = Split<N>::K;
 #pragma unroll
     for (int j = 0; j < N; ++j) {
         float s = T[j];
 #pragma unroll
-        for (int i = 1; i < N; ++i) s += T[i * N + j];
-        c[j] = s;
+        for (int i = 1; i < K; ++i) s += T[i * N + j];
+        c[j] = Pair<Split<N>::R>::sum(s);
     }
 }
 
@@ -111,20 +152,21 @@ __device__ __forceinline__ float col_residual(const float (&c)[N]) {
 // when a column is dominated by one entry close to 1.  At the optimum this is
 // also the Delta of eq (13) ([P] section 4.2).
 template <int N>
-__device__ __forceinline__ void hessian(const float (&T)[N * N], float (&h)[Tri<N>::S]) {
-    constexpr int M = N - 1;
+__device__ __forceinline__ void hessian(const float (&T)[Split<N>::K * N], float (&h)[Tri<N>::S]) {
+    constexpr int M = N - 1, K = Split<N>::K;
+    using P = Pair<Split<N>::R>;
 #pragma unroll
     for (int j = 0; j < M; ++j)
 #pragma unroll
         for (int k = 0; k < j; ++k) {
             float p = T[j] * T[k];
 #pragma unroll
-            for (int i = 1; i < N; ++i) p = fmaf(T[i * N + j], T[i * N + k], p);
-            h[Tri<N>::at(j, k)] = -p;
+            for (int i = 1; i < K; ++i) p = fmaf(T[i * N + j], T[i * N + k], p);
+            h[Tri<N>::at(j, k)] = -P::sum(p);
         }
     float dg[M];
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
+    for (int i = 0; i < K; ++i) {
         // o_j = sum of row i without entry j, from prefix and suffix sums
         float pre[N], suf[N];   // pre[k] = T_i0 + .. + T_i,k-1 (k >= 1); suf[k] = T_i,k+1 + .. (k <= N-2)
         pre[1] = T[i * N];
@@ -140,7 +182,7 @@ __device__ __forceinline__ void hessian(const float (&T)[N * N], float (&h)[Tri<
         }
     }
 #pragma unroll
-    for (int j = 0; j < M; ++j) h[Tri<N>::at(j, j)] = dg[j];
+    for (int j = 0; j < M; ++j) h[Tri<N>::at(j, j)] = P::sum(dg[j]);
 }
 
 // Adds 2^-22 tr(H) to the diagonal of the Newton system.  When some column of
@@ -246,9 +288,10 @@ struct SpdSolve<4> {
 // test) are accumulated row by row, and e, r are returned so that an accepted
 // trial is applied to T in place by accept_trial.  Returns f(x + s) - f(x).
 template <int N>
-__device__ __forceinline__ float trial_point(const float (&T)[N * N], const float (&s)[N - 1], float (&e)[N - 1],
-                                             float (&r)[N], float (&ct)[N]) {
-    constexpr int M = N - 1;
+__device__ __forceinline__ float trial_point(const float (&T)[Split<N>::K * N], const float (&s)[N - 1],
+                                             float (&e)[N - 1], float (&r)[Split<N>::K], float (&ct)[N]) {
+    constexpr int M = N - 1, K = Split<N>::K;
+    using P = Pair<Split<N>::R>;
     float em[M];
     float ssum = s[0];
 #pragma unroll
@@ -259,15 +302,16 @@ __device__ __forceinline__ float trial_point(const float (&T)[N * N], const floa
     }
     float q;   // prod_i (1 + a_i) - 1
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
+    for (int i = 0; i < K; ++i) {
         float t = T[i * N] * em[0];
 #pragma unroll
         for (int j = 1; j < M; ++j) t = fmaf(T[i * N + j], em[j], t);
         q = (i == 0) ? t : fmaf(q, t, q + t);
     }
+    q = P::prod_m1(q);
     float lsum = 0.0f;   // sum_i log2(rs_i), used when the step is not small
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
+    for (int i = 0; i < K; ++i) {
         float u[M];
         float rs = T[i * N + M];
 #pragma unroll
@@ -281,14 +325,17 @@ __device__ __forceinline__ float trial_point(const float (&T)[N * N], const floa
         for (int j = 0; j < M; ++j) ct[j] = (i == 0) ? u[j] * r[i] : ct[j] + u[j] * r[i];
         ct[M] = (i == 0) ? T[i * N + M] * r[i] : ct[M] + T[i * N + M] * r[i];
     }
-    return (fabsf(q) < 0.0625f ? log1p_series(q) : lsum * kLn2) - ssum;
+#pragma unroll
+    for (int j = 0; j < N; ++j) ct[j] = P::sum(ct[j]);
+    return (fabsf(q) < 0.0625f ? log1p_series(q) : P::sum(lsum) * kLn2) - ssum;
 }
 
 template <int N>
-__device__ __forceinline__ void accept_trial(float (&T)[N * N], const float (&e)[N - 1], const float (&r)[N]) {
-    constexpr int M = N - 1;
+__device__ __forceinline__ void accept_trial(float (&T)[Split<N>::K * N], const float (&e)[N - 1],
+                                             const float (&r)[Split<N>::K]) {
+    constexpr int M = N - 1, K = Split<N>::K;
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
+    for (int i = 0; i < K; ++i) {
 #pragma unroll
         for (int j = 0; j < M; ++j) T[i * N + j] = (T[i * N + j] * e[j]) * r[i];
         T[i * N + M] *= r[i];
@@ -301,10 +348,12 @@ __device__ __forceinline__ void accept_trial(float (&T)[N * N], const float (&e)
 // Base-2 units throughout; no column sum is ever formed, so an underflowed
 // column cannot produce log(0).
 template <int N>
-__device__ __forceinline__ void sinkhorn_sweep(const float (&L)[N * N], float (&y)[N - 1]) {
-    float a[N];
+__device__ __forceinline__ void sinkhorn_sweep(const float (&L)[Split<N>::K * N], float (&y)[N - 1]) {
+    constexpr int K = Split<N>::K;
+    using P = Pair<Split<N>::R>;
+    float a[K];
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
+    for (int i = 0; i < K; ++i) {
         float u[N];
 #pragma unroll
         for (int j = 0; j < N - 1; ++j) u[j] = L[i * N + j] + y[j];
@@ -320,16 +369,17 @@ __device__ __forceinline__ void sinkhorn_sweep(const float (&L)[N * N], float (&
     float z[N];
 #pragma unroll
     for (int j = 0; j < N; ++j) {
-        float v[N];
+        float v[K];
 #pragma unroll
-        for (int i = 0; i < N; ++i) v[i] = L[i * N + j] + a[i];
+        for (int i = 0; i < K; ++i) v[i] = L[i * N + j] + a[i];
         float m = v[0];
 #pragma unroll
-        for (int i = 1; i < N; ++i) m = fmaxf(m, v[i]);
+        for (int i = 1; i < K; ++i) m = fmaxf(m, v[i]);
+        m = P::max(m);
         float s = ex2(v[0] - m);
 #pragma unroll
-        for (int i = 1; i < N; ++i) s += ex2(v[i] - m);
-        z[j] = -(m + lg2(s));
+        for (int i = 1; i < K; ++i) s += ex2(v[i] - m);
+        z[j] = -(m + lg2(P::sum(s)));
     }
 #pragma unroll
     for (int j = 0; j < N - 1; ++j) y[j] = z[j] - z[N - 1];
@@ -341,43 +391,64 @@ __device__ __forceinline__ float step_size(int k) {
 }
 
 // ---------------------------------------------------------------------------
-// Kernel geometry.  A workgroup is kBlock lanes = kWaves waves; wave w of
-// workgroup g owns matrices [(g*kWaves + w)*64, +64), one per lane.  Matrix
-// I/O goes through the wave's private LDS tile (WaveTile), so every global
-// access instruction is fully coalesced; the dual (n floats per matrix) and
-// the iteration counts are already contiguous across lanes and are accessed
-// directly.  Lanes past the end of the batch compute on zeros and store
-// nothing; whole waves past the end return at once.
+// Kernel geometry.  A workgroup is kBlock lanes = kWaves waves.  Lane l of
+// wave w of workgroup g owns "item" (g*kWaves + w)*64 + l: rows
+// [h*K, (h+1)*K) of matrix item / R, h = item mod R.  Items are contiguous in
+// memory (K*n elements each), so a wave's items form one span; matrix I/O goes
+// through the wave's private LDS tile (WaveTile) so that every global access
+// instruction is coalesced.  The dual (n floats per matrix) and the iteration
+// counts are already contiguous across lanes and are accessed directly.
+// Lanes past the end of the batch compute on zeros and store nothing; whole
+// waves past the end return at once.
 // ---------------------------------------------------------------------------
 constexpr int kWaves = kBlock / 64;
 
 template <int N, typename IO>
 struct Geometry {
-    static constexpr int C = N * N * (int)sizeof(IO) / 16;   // 16-byte chunks per matrix
-    static_assert(C * 16 == N * N * (int)sizeof(IO), "matrix must be a whole number of 16-byte chunks");
+    static constexpr int R = Split<N>::R, K = Split<N>::K;
+    static constexpr int C = K * N * (int)sizeof(IO) / 16;   // 16-byte chunks per item
+    static_assert(C * 16 == K * N * (int)sizeof(IO), "an item must be a whole number of 16-byte chunks");
     using Tile = WaveTile<C>;
-    int lane, wave, nvalid;
-    int64_t base;   // first matrix of this wave
+    int lane, wave, nvalid;   // nvalid: items of this wave inside the batch (wave-uniform)
+    int64_t base;             // first item of this wave
     __device__ __forceinline__ Geometry(int64_t B) {
         lane = threadIdx.x & 63;
         wave = threadIdx.x >> 6;
         base = ((int64_t)blockIdx.x * kWaves + wave) * 64;
-        const int64_t left = B - base;
-        nvalid = __builtin_amdgcn_readfirstlane(left <= 0 ? 0 : left >= 64 ? 64 : (int)left);   // wave-uniform
+        const int64_t left = B * R - base;
+        nvalid = __builtin_amdgcn_readfirstlane(left <= 0 ? 0 : left >= 64 ? 64 : (int)left);
     }
+    __device__ __forceinline__ bool valid() const { return lane < nvalid; }
+    __device__ __forceinline__ int half() const { return lane & (R - 1); }            // which rows of the matrix
+    __device__ __forceinline__ int64_t matrix() const { return (base + lane) / R; }
+    __device__ __forceinline__ int64_t item() const { return base + lane; }
     __device__ __forceinline__ const uint4* chunks(const IO* p) const {
         return reinterpret_cast<const uint4*>(p) + base * C;
     }
     __device__ __forceinline__ uint4* chunks(IO* p) const { return reinterpret_cast<uint4*>(p) + base * C; }
 };
 
+// The dual entries [h*K, (h+1)*K) of matrix b, as K/4 16-byte stores.
 template <int N>
-__device__ __forceinline__ void store_dual(float* __restrict__ dual, int64_t b, const float (&beta)[N]) {
-    uint4* q = reinterpret_cast<uint4*>(dual + b * N);
+__device__ __forceinline__ void store_dual(float* __restrict__ dual, int64_t b, int h, const float (&beta)[N]) {
+    constexpr int K = Split<N>::K;
+    uint4* q = reinterpret_cast<uint4*>(dual + b * N + h * K);
 #pragma unroll
-    for (int k = 0; k < N / 4; ++k)
-        stream_store(q + k, make_uint4(__float_as_uint(beta[4 * k]), __float_as_uint(beta[4 * k + 1]),
-                                       __float_as_uint(beta[4 * k + 2]), __float_as_uint(beta[4 * k + 3])));
+    for (int k = 0; k < K / 4; ++k) {
+        uint4 v = make_uint4(__float_as_uint(beta[4 * k]), __float_as_uint(beta[4 * k + 1]),
+                             __float_as_uint(beta[4 * k + 2]), __float_as_uint(beta[4 * k + 3]));
+        if constexpr (Split<N>::R == 2) {
+            // the second lane of the pair stores the upper half (selected, not indexed by h,
+            // so that beta stays in registers)
+            const uint4 u = make_uint4(__float_as_uint(beta[K + 4 * k]), __float_as_uint(beta[K + 4 * k + 1]),
+                                       __float_as_uint(beta[K + 4 * k + 2]), __float_as_uint(beta[K + 4 * k + 3]));
+            v.x = h ? u.x : v.x;
+            v.y = h ? u.y : v.y;
+            v.z = h ? u.z : v.z;
+            v.w = h ? u.w : v.w;
+        }
+        stream_store(q + k, v);
+    }
 }
 
 template <int N>
@@ -393,64 +464,66 @@ __device__ __forceinline__ void load_dual(const float* __restrict__ dual, int64_
     }
 }
 
-// One lane reads its own matrix directly (used off the main path, where the
+// One lane reads its own item directly (used off the main path, where the
 // other lanes of the wave do not take part).
 template <int N, typename IO>
-__device__ __forceinline__ void load_own(const IO* __restrict__ p, int64_t b, float (&v)[N * N]) {
-    constexpr int C = N * N * (int)sizeof(IO) / 16;
-    const uint4* q = reinterpret_cast<const uint4*>(p) + b * C;
+__device__ __forceinline__ void load_own(const IO* __restrict__ p, int64_t item, float (&v)[Split<N>::K * N]) {
+    constexpr int KN = Split<N>::K * N;
+    constexpr int C = KN * (int)sizeof(IO) / 16;
+    const uint4* q = reinterpret_cast<const uint4*>(p) + item * C;
     uint4 w[C];
 #pragma unroll
     for (int k = 0; k < C; ++k) w[k] = q[k];
-    Storage<IO>::template decode<N * N>(w, v);
+    Storage<IO>::template decode<KN>(w, v);
 }
 
 // ---------------------------------------------------------------------------
-// Forward: Newton on the reduced dual (eq 8), one matrix per lane.
+// Forward: Newton on the reduced dual (eq 8).
 // ---------------------------------------------------------------------------
 
 // Loads the wave's logits, evaluates T at x^(0) = 0 and runs Newton's method to
-// column-sum residual <= tol or max_iter updates.  On return T is the last
-// iterate, y its dual (base-2 units, y_{N-1} = 0 implied), res its residual;
-// returns the number of updates.  The logits are needed again only by the
-// rare fallback sweep, which re-reads this lane's matrix; they do not stay in
-// registers through the loop.
+// column-sum residual <= tol or max_iter updates.  On return T is the lane's
+// rows of the last iterate, y the dual (base-2 units, y_{N-1} = 0 implied),
+// res its residual; returns the number of updates.  The logits are needed
+// again only by the rare fallback sweep, which re-reads this lane's rows; they
+// do not stay in registers through the loop.
 template <int N, typename IO, bool kPrefetch = false>
 __device__ __forceinline__ int newton_solve(const Geometry<N, IO>& geo, uint4* lds, const IO* __restrict__ logits,
-                                            float tol, int max_iter, float (&T_out)[N * N], float (&y_out)[N - 1],
-                                            float& res_out, const IO* __restrict__ prefetch_src = nullptr) {
-    constexpr int M = N - 1;
+                                            float tol, int max_iter, float (&T_out)[Split<N>::K * N],
+                                            float (&y_out)[N - 1], float& res_out,
+                                            const IO* __restrict__ prefetch_src = nullptr) {
+    constexpr int M = N - 1, K = Split<N>::K;
     using G = Geometry<N, IO>;
-    const int64_t b = geo.base + geo.lane;
     // the iteration works on locals, copied out at the end (keeps the loop in registers)
-    float T[N * N], y[M], c[N], res;
+    float T[K * N], y[M], c[N], res;
 #pragma unroll
     for (int j = 0; j < M; ++j) y[j] = 0.0f;   // x^(0) = 0
     {
-        float L[N * N];
+        float L[K * N];
         uint4 w[G::C];
         G::Tile::load(geo.chunks(logits), geo.nvalid * G::C, lds, geo.lane, w);
-        Storage<IO>::template decode<N * N>(w, L);
+        Storage<IO>::template decode<K * N>(w, L);
 #pragma unroll
-        for (int k = 0; k < N * N; ++k) L[k] *= kLog2e;
-        softmax_rows0<N>(L, T);
+        for (int k = 0; k < K * N; ++k) L[k] *= kLog2e;
+        softmax_rows0<N, K>(L, T);
     }
     // optionally start copying another tile of the wave (dL/dT) into the now
     // free LDS region, to be read after the iteration
     if constexpr (kPrefetch) G::Tile::prefetch(geo.chunks(prefetch_src), geo.nvalid * G::C, lds, geo.lane);
     col_sums<N>(T, c);
-    res = geo.lane < geo.nvalid ? col_residual<N>(c) : 0.0f;   // lanes past the end are done
+    res = geo.valid() ? col_residual<N>(c) : 0.0f;   // lanes past the end are done
     int it = 0;
 
     while (res > tol && it < max_iter) {
         float g[M], r[M], d[M];
-        float gn2 = 0.0f;
 #pragma unroll
         for (int j = 0; j < M; ++j) {
             g[j] = c[j] - 1.0f;
             r[j] = -g[j];
-            gn2 = fmaf(g[j], g[j], gn2);
         }
+        float gn2 = g[0] * g[0];
+#pragma unroll
+        for (int j = 1; j < M; ++j) gn2 = fmaf(g[j], g[j], gn2);
         float h[Tri<N>::S];
         hessian<N>(T, h);
         damp<N>(h);
@@ -460,7 +533,7 @@ __device__ __forceinline__ int newton_solve(const Geometry<N, IO>& geo, uint4* l
         if (ok) {
             for (int k = 0; k < 5; ++k) {
                 const float gam = step_size(k);
-                float s[M], e[M], rr[N], ct[N];
+                float s[M], e[M], rr[K], ct[N];
 #pragma unroll
                 for (int j = 0; j < M; ++j) s[j] = gam * d[j];
                 const float df = trial_point<N>(T, s, e, rr, ct);
@@ -479,75 +552,78 @@ __device__ __forceinline__ int newton_solve(const Geometry<N, IO>& geo, uint4* l
             }
         }
         if (!accepted) {
-            float L[N * N];
-            load_own<N, IO>(logits, b, L);
+            float L[K * N];
+            load_own<N, IO>(logits, geo.item(), L);
 #pragma unroll
-            for (int k = 0; k < N * N; ++k) L[k] *= kLog2e;
+            for (int k = 0; k < K * N; ++k) L[k] *= kLog2e;
             sinkhorn_sweep<N>(L, y);
-            softmax_rows<N>(L, y, T);
+            softmax_rows<N, K>(L, y, T);
             col_sums<N>(T, c);
         }
         ++it;
         res = col_residual<N>(c);
     }
 #pragma unroll
-    for (int k = 0; k < N * N; ++k) T_out[k] = T[k];
+    for (int k = 0; k < K * N; ++k) T_out[k] = T[k];
 #pragma unroll
     for (int j = 0; j < M; ++j) y_out[j] = y[j];
     res_out = res;
     return it;
 }
 
-// Writes the wave's T through its LDS tile and, per valid lane, the dual
-// (natural units, beta_{N-1} = 0).
+// Writes the wave's T through its LDS tile and, per valid lane, the lane's
+// share of the dual (natural units, beta_{N-1} = 0).
 template <int N, typename IO>
 __device__ __forceinline__ void store_forward(const Geometry<N, IO>& geo, uint4* lds, IO* __restrict__ Tout,
-                                              float* __restrict__ dual, const float (&T)[N * N],
+                                              float* __restrict__ dual, const float (&T)[Split<N>::K * N],
                                               const float (&y)[N - 1]) {
     using G = Geometry<N, IO>;
     {
         uint4 w[G::C];
-        Storage<IO>::template encode<N * N>(T, w);
+        Storage<IO>::template encode<G::K * N>(T, w);
         G::Tile::store(w, lds, geo.lane, geo.chunks(Tout), geo.nvalid * G::C);
     }
-    if (geo.lane < geo.nvalid) {
+    if (geo.valid()) {
         float beta[N];
 #pragma unroll
         for (int j = 0; j < N - 1; ++j) beta[j] = y[j] * kLn2;
         beta[N - 1] = 0.0f;
-        store_dual<N>(dual, geo.base + geo.lane, beta);
+        store_dual<N>(dual, geo.matrix(), geo.half(), beta);
     }
 }
 
 template <int N, typename IO, bool kStats>
-__global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(N == 4 ? 7 : 1)))
+__global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(N == 4 ? 7 : 4)))
 newton_fwd_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, float* __restrict__ dual,
                   int32_t* __restrict__ iters, int64_t B, float tol, int max_iter) {
     using G = Geometry<N, IO>;
     __shared__ uint4 lds[kWaves][G::Tile::kLdsChunks];
     const G geo(B);
     if (geo.nvalid == 0) return;
-    float T[N * N], y[N - 1], res;
+    float T[G::K * N], y[N - 1], res;
     const int it = newton_solve<N, IO>(geo, lds[geo.wave], logits, tol, max_iter, T, y, res);
     store_forward<N, IO>(geo, lds[geo.wave], Tout, dual, T, y);
-    if (kStats && geo.lane < geo.nvalid) iters[geo.base + geo.lane] = (res <= tol) ? it : -1;
+    if (kStats && geo.valid() && geo.half() == 0) iters[geo.matrix()] = (res <= tol) ? it : -1;
 }
 
 // ---------------------------------------------------------------------------
-// Backward: eq (13), one matrix per lane.
+// Backward: eq (13).
 // ---------------------------------------------------------------------------
 
-// dH = d<G, T>/dH at the projection T, for upstream G = dL/dT.  eq (13) with
-// eta = 1, a = b = 1 and the sign flipped for H = -M ([P] section 4.2):
+// dH = d<G, T>/dH at the projection T, for upstream G = dL/dT (the lane's K
+// rows of each).  eq (13) with eta = 1, a = b = 1 and the sign flipped for
+// H = -M ([P] section 4.2):
 //   mu_r = (G o T) 1,  rhs = mu_c - T_{-n}^T mu_r = sum_i T_ij (G_ij - mu_r_i),
 //   Delta = I - T_{-n}^T T_{-n} (the Hessian at the optimum), w_{-n} = Delta^{-1} rhs, w_n = 0,
 //   v = mu_r - T_{-n} w_{-n},  dH = -D = (G - v 1^T - 1 w^T) o T.
 template <int N>
-__device__ __forceinline__ void implicit_grad(const float (&T)[N * N], const float (&G)[N * N], float (&out)[N * N]) {
-    constexpr int M = N - 1;
-    float mur[N];
+__device__ __forceinline__ void implicit_grad(const float (&T)[Split<N>::K * N], const float (&G)[Split<N>::K * N],
+                                              float (&out)[Split<N>::K * N]) {
+    constexpr int M = N - 1, K = Split<N>::K;
+    using P = Pair<Split<N>::R>;
+    float mur[K];
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
+    for (int i = 0; i < K; ++i) {
         float s = G[i * N] * T[i * N];
 #pragma unroll
         for (int j = 1; j < N; ++j) s = fmaf(G[i * N + j], T[i * N + j], s);
@@ -558,14 +634,14 @@ __device__ __forceinline__ void implicit_grad(const float (&T)[N * N], const flo
     for (int j = 0; j < M; ++j) {
         float s = T[j] * (G[j] - mur[0]);
 #pragma unroll
-        for (int i = 1; i < N; ++i) s = fmaf(T[i * N + j], G[i * N + j] - mur[i], s);
-        rhs[j] = s;
+        for (int i = 1; i < K; ++i) s = fmaf(T[i * N + j], G[i * N + j] - mur[i], s);
+        rhs[j] = P::sum(s);
     }
     float h[Tri<N>::S], w[M];
     hessian<N>(T, h);
     SpdSolve<N>::run(h, rhs, w);
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
+    for (int i = 0; i < K; ++i) {
         float v = mur[i];
 #pragma unroll
         for (int j = 0; j < M; ++j) v = fmaf(-T[i * N + j], w[j], v);
@@ -585,43 +661,41 @@ implicit_bwd_kernel(const IO* __restrict__ logits, const float* __restrict__ dua
                     IO* __restrict__ dH, int64_t B) {
     constexpr int M = N - 1;
     using Gm = Geometry<N, IO>;
-    constexpr int C = Gm::C;
+    constexpr int C = Gm::C, K = Gm::K;
     __shared__ uint4 lds[kWaves][Gm::Tile::kLdsChunks];
     const Gm geo(B);
     if (geo.nvalid == 0) return;
-    const bool valid = geo.lane < geo.nvalid;
-    const int64_t b = geo.base + geo.lane;
 
     // issue every global load first, then route the chunks to their owners
     uint4 th[C], tg[C];
     Gm::Tile::fetch(geo.chunks(logits), geo.nvalid * C, geo.lane, th);
     Gm::Tile::fetch(geo.chunks(dT), geo.nvalid * C, geo.lane, tg);
     float beta[N];
-    if (valid)
-        load_dual<N>(dual, b, beta);
+    if (geo.valid())
+        load_dual<N>(dual, geo.matrix(), beta);
     else
 #pragma unroll
         for (int j = 0; j < N; ++j) beta[j] = 0.0f;
-    float L[N * N], G[N * N];
+    float L[K * N], G[K * N];
     {
         uint4 w[C];
         Gm::Tile::route(th, lds[geo.wave], geo.lane, w);
-        Storage<IO>::template decode<N * N>(w, L);
+        Storage<IO>::template decode<K * N>(w, L);
         Gm::Tile::route(tg, lds[geo.wave], geo.lane, w);
-        Storage<IO>::template decode<N * N>(w, G);
+        Storage<IO>::template decode<K * N>(w, G);
     }
 #pragma unroll
-    for (int k = 0; k < N * N; ++k) L[k] *= kLog2e;
+    for (int k = 0; k < K * N; ++k) L[k] *= kLog2e;
     float y[M];
 #pragma unroll
     for (int j = 0; j < M; ++j) y[j] = (beta[j] - beta[M]) * kLog2e;   // T is invariant to the gauge
-    float T[N * N];
-    softmax_rows<N>(L, y, T);
-    float out[N * N];
+    float T[K * N];
+    softmax_rows<N, K>(L, y, T);
+    float out[K * N];
     implicit_grad<N>(T, G, out);
     {
         uint4 wo[C];
-        Storage<IO>::template encode<N * N>(out, wo);
+        Storage<IO>::template encode<K * N>(out, wo);
         Gm::Tile::store(wo, lds[geo.wave], geo.lane, geo.chunks(dH), geo.nvalid * C);
     }
 }
@@ -633,25 +707,25 @@ __global__ void __launch_bounds__(kBlock)
 implicit_bwd_from_T_kernel(const float* __restrict__ Tin, const float* __restrict__ dT, float* __restrict__ dH,
                            int64_t B) {
     using Gm = Geometry<N, float>;
-    constexpr int C = Gm::C;
+    constexpr int C = Gm::C, K = Gm::K;
     __shared__ uint4 lds[kWaves][Gm::Tile::kLdsChunks];
     const Gm geo(B);
     if (geo.nvalid == 0) return;
     uint4 tt[C], tg[C];
     Gm::Tile::fetch(geo.chunks(Tin), geo.nvalid * C, geo.lane, tt);
     Gm::Tile::fetch(geo.chunks(dT), geo.nvalid * C, geo.lane, tg);
-    float T[N * N], G[N * N], out[N * N];
+    float T[K * N], G[K * N], out[K * N];
     {
         uint4 w[C];
         Gm::Tile::route(tt, lds[geo.wave], geo.lane, w);
-        Storage<float>::template decode<N * N>(w, T);
+        Storage<float>::template decode<K * N>(w, T);
         Gm::Tile::route(tg, lds[geo.wave], geo.lane, w);
-        Storage<float>::template decode<N * N>(w, G);
+        Storage<float>::template decode<K * N>(w, G);
     }
     implicit_grad<N>(T, G, out);
     {
         uint4 wo[C];
-        Storage<float>::template encode<N * N>(out, wo);
+        Storage<float>::template encode<K * N>(out, wo);
         Gm::Tile::store(wo, lds[geo.wave], geo.lane, geo.chunks(dH), geo.nvalid * C);
     }
 }
@@ -663,22 +737,22 @@ implicit_bwd_from_T_kernel(const float* __restrict__ Tin, const float* __restric
 // read back.  Reads logits and dT, writes T, dual and dH.
 // ---------------------------------------------------------------------------
 template <int N, typename IO>
-__global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(N == 4 ? 6 : 1)))
+__global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(N == 4 ? 6 : 4)))
 fused_fwd_bwd_kernel(const IO* __restrict__ logits, const IO* __restrict__ dT, IO* __restrict__ Tout,
                      float* __restrict__ dual, IO* __restrict__ dH, int64_t B, float tol, int max_iter) {
     using Gm = Geometry<N, IO>;
-    constexpr int C = Gm::C;
+    constexpr int C = Gm::C, K = Gm::K;
     __shared__ uint4 lds[kWaves][Gm::Tile::kLdsChunks];
     const Gm geo(B);
     if (geo.nvalid == 0) return;
-    float T[N * N], y[N - 1], res;
-    float G[N * N], out[N * N];
+    float T[K * N], y[N - 1], res;
+    float G[K * N], out[K * N];
     if constexpr (Gm::Tile::kStaged) {
         // dL/dT travels into LDS while the Newton iteration runs
         newton_solve<N, IO, true>(geo, lds[geo.wave], logits, tol, max_iter, T, y, res, dT);
         uint4 w[C];
         Gm::Tile::read_prefetched(lds[geo.wave], geo.lane, w);
-        Storage<IO>::template decode<N * N>(w, G);
+        Storage<IO>::template decode<K * N>(w, G);
         store_forward<N, IO>(geo, lds[geo.wave], Tout, dual, T, y);
     } else {
         newton_solve<N, IO>(geo, lds[geo.wave], logits, tol, max_iter, T, y, res);
@@ -687,12 +761,12 @@ fused_fwd_bwd_kernel(const IO* __restrict__ logits, const IO* __restrict__ dT, I
         store_forward<N, IO>(geo, lds[geo.wave], Tout, dual, T, y);
         uint4 w[C];
         Gm::Tile::route(tg, lds[geo.wave], geo.lane, w);
-        Storage<IO>::template decode<N * N>(w, G);
+        Storage<IO>::template decode<K * N>(w, G);
     }
     implicit_grad<N>(T, G, out);
     {
         uint4 wo[C];
-        Storage<IO>::template encode<N * N>(out, wo);
+        Storage<IO>::template encode<K * N>(out, wo);
         Gm::Tile::store(wo, lds[geo.wave], geo.lane, geo.chunks(dH), geo.nvalid * C);
     }
 }
@@ -704,26 +778,27 @@ template <int N, typename IO>
 __global__ void __launch_bounds__(kBlock)
 sinkhorn_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, int64_t B, int sweeps) {
     using G = Geometry<N, IO>;
+    constexpr int K = G::K;
+    using P = Pair<G::R>;
     __shared__ uint4 lds[kWaves][G::Tile::kLdsChunks];
     const G geo(B);
     if (geo.nvalid == 0) return;
-    float L[N * N];
+    float L[K * N];
     {
         uint4 w[G::C];
         G::Tile::load(geo.chunks(logits), geo.nvalid * G::C, lds[geo.wave], geo.lane, w);
-        Storage<IO>::template decode<N * N>(w, L);
+        Storage<IO>::template decode<K * N>(w, L);
     }
 #pragma unroll
-    for (int k = 0; k < N * N; ++k) L[k] *= kLog2e;
-    float a[N], z[N];
+    for (int k = 0; k < K * N; ++k) L[k] *= kLog2e;
+    float a[K], z[N];
 #pragma unroll
-    for (int j = 0; j < N; ++j) {
-        a[j] = 0.0f;
-        z[j] = 0.0f;   // v^(0) = 1
-    }
+    for (int i = 0; i < K; ++i) a[i] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < N; ++j) z[j] = 0.0f;   // v^(0) = 1
     for (int t = 0; t < sweeps; ++t) {
 #pragma unroll
-        for (int i = 0; i < N; ++i) {   // u = 1 / (A v): alpha_i = -LSE_j(H_ij + beta_j)
+        for (int i = 0; i < K; ++i) {   // u = 1 / (A v): alpha_i = -LSE_j(H_ij + beta_j)
             float u[N];
 #pragma unroll
             for (int j = 0; j < N; ++j) u[j] = L[i * N + j] + z[j];
@@ -737,26 +812,27 @@ sinkhorn_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, int64_t B,
         }
 #pragma unroll
         for (int j = 0; j < N; ++j) {   // v = 1 / (A^T u): beta_j = -LSE_i(H_ij + alpha_i)
-            float v[N];
+            float v[K];
 #pragma unroll
-            for (int i = 0; i < N; ++i) v[i] = L[i * N + j] + a[i];
+            for (int i = 0; i < K; ++i) v[i] = L[i * N + j] + a[i];
             float m = v[0];
 #pragma unroll
-            for (int i = 1; i < N; ++i) m = fmaxf(m, v[i]);
+            for (int i = 1; i < K; ++i) m = fmaxf(m, v[i]);
+            m = P::max(m);
             float s = ex2(v[0] - m);
 #pragma unroll
-            for (int i = 1; i < N; ++i) s += ex2(v[i] - m);
-            z[j] = -(m + lg2(s));
+            for (int i = 1; i < K; ++i) s += ex2(v[i] - m);
+            z[j] = -(m + lg2(P::sum(s)));
         }
     }
-    float T[N * N];
+    float T[K * N];
 #pragma unroll
-    for (int i = 0; i < N; ++i)
+    for (int i = 0; i < K; ++i)
 #pragma unroll
         for (int j = 0; j < N; ++j) T[i * N + j] = ex2(L[i * N + j] + a[i] + z[j]);
     {
         uint4 w[G::C];
-        Storage<IO>::template encode<N * N>(T, w);
+        Storage<IO>::template encode<K * N>(T, w);
         G::Tile::store(w, lds[geo.wave], geo.lane, geo.chunks(Tout), geo.nvalid * G::C);
     }
 }

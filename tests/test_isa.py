@@ -1,0 +1,62 @@
+"""Code-generation checks on the gfx950 assembly of the kernels (CPU only: hipcc
+cross-compiles).  They pin properties the measured performance depends on:
+every matrix / dual store is non-temporal, the n = 4 kernels keep their
+occupancy and spill nothing, and the n = 8 loops keep four waves per SIMD."""
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from birkhoff_projection_amd import build as hipbuild
+
+pytestmark = pytest.mark.skipif(shutil.which("hipcc") is None and not hipbuild.os.path.exists("/opt/rocm/bin/hipcc"),
+                                reason="hipcc not available")
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    out = tmp_path_factory.mktemp("isa") / "birkhoff.s"
+    cmd = [hipbuild.hipcc(), "--offload-arch=%s" % hipbuild.ARCH, "-O3", "-std=c++17",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", str(hipbuild.ROOT / "include"), "-I", str(hipbuild.CSRC),
+           "--cuda-device-only", "-S", str(hipbuild.SOURCES[0]), "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return out.read_text()
+
+
+def kernels(asm):
+    """{mangled kernel name: (body text, vgprs, scratch bytes, occupancy)}"""
+    out = {}
+    for m in re.finditer(r"^(_ZN4birk\w+):.*?\n(.*?)^; Occupancy: (\d+)", asm, flags=re.M | re.S):
+        body = m.group(2)
+        vgpr = int(re.search(r"; TotalNumVgprs: (\d+)", body).group(1))
+        scratch = int(re.search(r"; ScratchSize: (\d+)", body).group(1))
+        out[m.group(1)] = (body, vgpr, scratch, int(m.group(3)))
+    return out
+
+
+def test_all_global_stores_are_non_temporal(asm):
+    ks = kernels(asm)
+    assert ks
+    for name, (body, *_rest) in ks.items():
+        for line in re.findall(r"^\s+global_store_dwordx4.*$", body, flags=re.M):
+            assert line.rstrip().endswith(" nt"), (name, line)
+
+
+def test_n4_kernels_occupancy_and_no_spills(asm):
+    ks = kernels(asm)
+    want = {"newton_fwd_kernelILi4Ef": 7, "fused_fwd_bwd_kernelILi4Ef": 6, "implicit_bwd_kernelILi4Ef": 7}
+    for key, occ in want.items():
+        hits = [v for k, v in ks.items() if key in k]
+        assert hits, key
+        for _, vgpr, scratch, o in hits:
+            assert scratch == 0 and o >= occ, (key, vgpr, scratch, o)
+
+
+def test_n8_forward_keeps_four_waves(asm):
+    ks = kernels(asm)
+    hits = [v for k, v in ks.items() if "newton_fwd_kernelILi8Ef" in k or "fused_fwd_bwd_kernelILi8Ef" in k]
+    assert hits
+    for _, vgpr, scratch, o in hits:
+        assert o >= 4, (vgpr, scratch, o)
