@@ -11,7 +11,8 @@ numpy arrays through ctypes.  See the header of ``oracle.c`` for the passages
 of "Accelerating Birkhoff Projection for Manifold-Constrained
 Hyper-Connections" that each function follows.
 
-All functions take float64 arrays of shape [B, n, n] (row-major) and return
+The Birkhoff functions take float64 arrays of shape [B, n, n] (row-major); the
+eot_* functions take a cost [B, n, m] with marginals a, b and eta.  All return
 float64 arrays.  Inputs stored as fp32 or bf16 are decoded exactly to float64
 by the caller before they get here.
 """
@@ -73,6 +74,16 @@ def _load():
     lib.oracle_bwd.argtypes = [dp, dp, i64, ci, dp]
     lib.oracle_residuals.restype = ci
     lib.oracle_residuals.argtypes = [dp, i64, ci, dp]
+    lib.oracle_eot_sinkhorn_tol.restype = ci
+    lib.oracle_eot_sinkhorn_tol.argtypes = [dp, dp, dp, i64, ci, ci, cd, cd, ci, dp, dp, ip, ip]
+    lib.oracle_eot_newton.restype = ci
+    lib.oracle_eot_newton.argtypes = [dp, dp, dp, i64, ci, ci, cd, cd, ci, dp, dp, ip]
+    lib.oracle_eot_project.restype = ci
+    lib.oracle_eot_project.argtypes = [dp, dp, dp, i64, ci, ci, cd, ci, dp, dp, ip]
+    lib.oracle_eot_bwd.restype = ci
+    lib.oracle_eot_bwd.argtypes = [dp, dp, dp, dp, i64, ci, ci, cd, dp]
+    lib.oracle_eot_residuals.restype = ci
+    lib.oracle_eot_residuals.argtypes = [dp, dp, dp, i64, ci, ci, dp]
     _lib = lib
     return lib
 
@@ -172,4 +183,78 @@ def residuals(T):
     B, n, _ = T.shape
     r = np.empty(B)
     _check(_load().oracle_residuals(_p(T), B, n, _p(r)), "residuals")
+    return r
+
+
+# ---------------------------------------------------------------------------
+# General small entropic OT: cost M [B, n, m], marginals a [B, n], b [B, m]
+# (or [n], [m], shared by every problem), regularisation eta > 0.
+# ---------------------------------------------------------------------------
+
+def _eot_args(M, a, b):
+    M = np.ascontiguousarray(np.asarray(M, dtype=np.float64))
+    if M.ndim == 2:
+        M = M[None]
+    if M.ndim != 3:
+        raise ValueError("expected a cost of shape [B, n, m] or [n, m], got %r" % (M.shape,))
+    B, n, m = M.shape
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    a = np.ascontiguousarray(np.broadcast_to(a, (B, n)))
+    b = np.ascontiguousarray(np.broadcast_to(b, (B, m)))
+    return M, a, b, B, n, m
+
+
+def eot_project(M, a, b, eta: float = 1.0, sk_cap: int = SK_CAP_DEFAULT):
+    """Reference plan of min <T, M> - eta h(T) over T with T 1 = a, T^T 1 = b.
+
+    Returns (T [B,n,m], beta [B,m] with beta_m = 0, status [B]); status as in
+    project()."""
+    M, a, b, B, n, m = _eot_args(M, a, b)
+    T = np.empty_like(M)
+    beta = np.empty((B, m))
+    st = np.empty(B, dtype=np.int32)
+    _check(_load().oracle_eot_project(_p(M), _p(a), _p(b), B, n, m, float(eta), int(sk_cap), _p(T), _p(beta),
+                                      _p(st, ctypes.c_int32)), "eot_project")
+    return T, beta, st
+
+
+def eot_sinkhorn_tol(M, a, b, eta: float = 1.0, tol: float = 1e-13, cap: int = SK_CAP_DEFAULT):
+    """Sinkhorn-Knopp (eq 7) to marginal residual <= tol. Returns (T, beta, sweeps, converged)."""
+    M, a, b, B, n, m = _eot_args(M, a, b)
+    T = np.empty_like(M)
+    beta = np.empty((B, m))
+    sw = np.empty(B, dtype=np.int32)
+    cv = np.empty(B, dtype=np.int32)
+    _check(_load().oracle_eot_sinkhorn_tol(_p(M), _p(a), _p(b), B, n, m, float(eta), float(tol), int(cap), _p(T),
+                                           _p(beta), _p(sw, ctypes.c_int32), _p(cv, ctypes.c_int32)),
+           "eot_sinkhorn_tol")
+    return T, beta, sw, cv.astype(bool)
+
+
+def eot_newton(M, a, b, eta: float = 1.0, tol: float = 1e-13, max_iter: int = 500):
+    """float64 Newton on the reduced dual of eq (8). Returns (T, beta, iters); iters -1 = tol not met."""
+    M, a, b, B, n, m = _eot_args(M, a, b)
+    T = np.empty_like(M)
+    beta = np.empty((B, m))
+    it = np.empty(B, dtype=np.int32)
+    _check(_load().oracle_eot_newton(_p(M), _p(a), _p(b), B, n, m, float(eta), float(tol), int(max_iter), _p(T),
+                                     _p(beta), _p(it, ctypes.c_int32)), "eot_newton")
+    return T, beta, it
+
+
+def eot_bwd(T, G, a, b, eta: float = 1.0):
+    """eq (13): D = d<G, T*>/dM at plans T with upstream G."""
+    T, a, b, B, n, m = _eot_args(T, a, b)
+    G = np.ascontiguousarray(np.asarray(G, dtype=np.float64)).reshape(T.shape)
+    D = np.empty_like(T)
+    _check(_load().oracle_eot_bwd(_p(T), _p(G), _p(a), _p(b), B, n, m, float(eta), _p(D)), "eot_bwd")
+    return D
+
+
+def eot_residuals(T, a, b):
+    """Per-problem max(|T 1 - a|, |T^T 1 - b|), summed in double."""
+    T, a, b, B, n, m = _eot_args(T, a, b)
+    r = np.empty(B)
+    _check(_load().oracle_eot_residuals(_p(T), _p(a), _p(b), B, n, m, _p(r)), "eot_residuals")
     return r

@@ -25,6 +25,17 @@
  * Precision.  Everything is IEEE double; no -ffast-math.  Plain libm exp,
  * log, expm1 and log1p.
  *
+ * The oracle_eot_* functions cover the general small entropic OT of [P]
+ * section 2.3 (cost M, marginals a and b, regularisation eta, n x m) with the
+ * same algorithms: Sinkhorn-Knopp as the block coordinate ascent of eq (7),
+ * Newton on eq (8) with the gradient and Hessian of eq (9), eq (13) backward.
+ * Their pins: a hand-worked 2 x 2 plan, the 2 x 2 quadratic closed form, the
+ * product plan of a separable cost, the optimality certificate of eq (4), a
+ * constrained primal solver for eq (3), a library minimiser for eq (8), a
+ * finite-difference Newton step, the eta / transpose / marginal-scaling
+ * symmetries, the Birkhoff special case, finite differences, shift invariants
+ * and unrolled autograd for eq (13).
+ *
  * Parity pins.  Every exported function is pinned by tests that do not call
  * this code for the expected value: the n = 2 closed form, exactly known
  * fixed points (doubly stochastic inputs with row/column shifts), rank-one
@@ -366,6 +377,233 @@ static int bwd_one(const double *T, const double *G, int n, double *dH)
 }
 
 /* ------------------------------------------------------------------ */
+/* General small entropic OT ([P] section 2.3, eqs (3)-(9); eq (13))    */
+/* ------------------------------------------------------------------ */
+/* Cost M is n x m (row-major), marginals a (n) > 0 and b (m) > 0 with equal
+ * sums, regularisation eta > 0.  The plan is T_ij = exp((alpha_i + beta_j -
+ * M_ij) / eta) (eq 4), the dual reported with beta_m = 0. */
+
+/* eq (5): alpha_i = eta log a_i - eta log sum_j exp((beta_j - M_ij) / eta) */
+static void eot_alpha(const double *M, const double *a, int n, int m, double eta, const double *beta,
+                      double *alpha)
+{
+    double u[ORACLE_NMAX];
+    for (int i = 0; i < n; ++i) {
+        for (int j = 0; j < m; ++j) u[j] = (beta[j] - M[i * m + j]) / eta;
+        alpha[i] = eta * log(a[i]) - eta * lse(u, m, 1);
+    }
+}
+
+/* eq (6): beta_j = eta log b_j - eta log sum_i exp((alpha_i - M_ij) / eta) */
+static void eot_beta(const double *M, const double *b, int n, int m, double eta, const double *alpha,
+                     double *beta)
+{
+    double u[ORACLE_NMAX];
+    for (int j = 0; j < m; ++j) {
+        for (int i = 0; i < n; ++i) u[i] = (alpha[i] - M[i * m + j]) / eta;
+        beta[j] = eta * log(b[j]) - eta * lse(u, n, 1);
+    }
+}
+
+/* primal recovery after eq (4) */
+static void eot_primal(const double *M, int n, int m, double eta, const double *alpha, const double *beta,
+                       double *T)
+{
+    for (int i = 0; i < n; ++i)
+        for (int j = 0; j < m; ++j) T[i * m + j] = exp((alpha[i] + beta[j] - M[i * m + j]) / eta);
+}
+
+/* max(|T 1 - a|, |T^T 1 - b|) */
+static double eot_marginal_residual(const double *T, const double *a, const double *b, int n, int m)
+{
+    double r = 0.0;
+    for (int i = 0; i < n; ++i) {
+        double s = 0.0;
+        for (int j = 0; j < m; ++j) s += T[i * m + j];
+        double e = fabs(s - a[i]);
+        if (!(e <= r)) r = e;
+    }
+    for (int j = 0; j < m; ++j) {
+        double s = 0.0;
+        for (int i = 0; i < n; ++i) s += T[i * m + j];
+        double e = fabs(s - b[j]);
+        if (!(e <= r)) r = e;
+    }
+    return r;
+}
+
+/* Block coordinate ascent eq (7) (= Sinkhorn-Knopp) from beta = 0 until the
+ * marginal residual is <= tol, at most cap sweeps. */
+static int eot_sk_one(const double *M, const double *a, const double *b, int n, int m, double eta, double tol,
+                      int cap, double *T, double *beta_out, int *conv)
+{
+    double alpha[ORACLE_NMAX], beta[ORACLE_NMAX];
+    for (int j = 0; j < m; ++j) beta[j] = 0.0;
+    *conv = 0;
+    int k = 0;
+    while (k < cap) {
+        ++k;
+        eot_alpha(M, a, n, m, eta, beta, alpha);
+        eot_beta(M, b, n, m, eta, alpha, beta);
+        eot_primal(M, n, m, eta, alpha, beta, T);
+        if (eot_marginal_residual(T, a, b, n, m) <= tol) { *conv = 1; break; }
+    }
+    if (k == 0) {
+        eot_alpha(M, a, n, m, eta, beta, alpha);
+        eot_primal(M, n, m, eta, alpha, beta, T);
+    }
+    for (int j = 0; j < m; ++j) beta_out[j] = beta[j] - beta[m - 1];
+    return k;
+}
+
+/* T(beta): T_i. = a_i Softmax((beta - M_i.) / eta) ([P] section 3.1); c = T^T 1. */
+static void eot_eval_T(const double *M, const double *a, int n, int m, double eta, const double *beta, double *T,
+                       double *c)
+{
+    for (int i = 0; i < n; ++i) {
+        double mu = -INFINITY;
+        for (int j = 0; j < m; ++j) {
+            double u = (beta[j] - M[i * m + j]) / eta;
+            if (u > mu) mu = u;
+        }
+        double s = 0.0;
+        for (int j = 0; j < m; ++j) {
+            double e = exp((beta[j] - M[i * m + j]) / eta - mu);
+            T[i * m + j] = e;
+            s += e;
+        }
+        for (int j = 0; j < m; ++j) T[i * m + j] *= a[i] / s;
+    }
+    for (int j = 0; j < m; ++j) {
+        double s = 0.0;
+        for (int i = 0; i < n; ++i) s += T[i * m + j];
+        c[j] = s;
+    }
+}
+
+/* Newton's method on the reduced dual (eq 8), from x = 0:
+ *   gradient  g = c_{-m} - b_{-m}                                   (eq 9)
+ *   Hessian   eta^-1 [diag(c_{-m}) - T_{-m}^T diag(a)^-1 T_{-m}]    (eq 9)
+ * with the step-size rule and Sinkhorn fallback of [B] section 2.2, as in
+ * newton_one.  With S_i. = T_i. / a_i (row softmaxes) the objective change is
+ *   f(x + s) - f(x) = eta sum_i a_i log(sum_j S_ij e^{s_j / eta}) - sum_j s_j b_j
+ * (eq 8 with eq 5), written with log1p / expm1.  Stops when every column sum
+ * is within tol of b (rows are exact by construction).  Returns the number of
+ * updates, or -1 when tol was not reached. */
+static int eot_newton_one(const double *M, const double *a, const double *b, int n, int m, double eta, double tol,
+                          int max_iter, double *T, double *beta_out)
+{
+    static const double steps[5] = {1.0, 0.5, 0.1, 0.05, 0.01};
+    const int k1 = m - 1;
+    double beta[ORACLE_NMAX], c[ORACLE_NMAX], g[ORACLE_NMAX], d[ORACLE_NMAX];
+    double hess[ORACLE_NMAX * ORACLE_NMAX];
+    double bt[ORACLE_NMAX], Tt[ORACLE_NMAX * ORACLE_NMAX], ct[ORACLE_NMAX];
+    double alpha[ORACLE_NMAX];
+    for (int j = 0; j < m; ++j) beta[j] = 0.0;
+    eot_eval_T(M, a, n, m, eta, beta, T, c);
+    int it = 0, conv = 0;
+    for (;;) {
+        double res = 0.0;
+        for (int j = 0; j < m; ++j) {
+            double e = fabs(c[j] - b[j]);
+            if (!(e <= res)) res = e;
+        }
+        if (res != res) break;
+        if (res <= tol) { conv = 1; break; }
+        if (it >= max_iter) break;
+
+        double gn2 = 0.0;
+        for (int j = 0; j < k1; ++j) { g[j] = c[j] - b[j]; gn2 += g[j] * g[j]; }
+        for (int j = 0; j < k1; ++j)
+            for (int k = 0; k < k1; ++k) {
+                double p = 0.0;
+                for (int i = 0; i < n; ++i) p += T[i * m + j] * T[i * m + k] / a[i];
+                hess[j * k1 + k] = ((j == k ? c[j] : 0.0) - p) / eta;
+            }
+        for (int j = 0; j < k1; ++j) d[j] = -g[j];
+        int accepted = 0;
+        if (solve_gepp(hess, d, k1) == 0) {
+            for (int st = 0; st < 5 && !accepted; ++st) {
+                double gam = steps[st];
+                double df = 0.0;
+                for (int i = 0; i < n; ++i) {
+                    double acc = 0.0;
+                    for (int j = 0; j < k1; ++j) acc += T[i * m + j] / a[i] * expm1(gam * d[j] / eta);
+                    df += eta * a[i] * log1p(acc);
+                }
+                for (int j = 0; j < k1; ++j) df -= gam * d[j] * b[j];
+                for (int j = 0; j < k1; ++j) bt[j] = beta[j] + gam * d[j];
+                bt[k1] = 0.0;
+                eot_eval_T(M, a, n, m, eta, bt, Tt, ct);
+                double gt2 = 0.0;
+                for (int j = 0; j < k1; ++j) gt2 += (ct[j] - b[j]) * (ct[j] - b[j]);
+                if (df < 0.0 && gt2 < gn2) {
+                    accepted = 1;
+                    memcpy(beta, bt, sizeof(double) * m);
+                    memcpy(T, Tt, sizeof(double) * n * m);
+                    memcpy(c, ct, sizeof(double) * m);
+                }
+            }
+        }
+        if (!accepted) {
+            eot_alpha(M, a, n, m, eta, beta, alpha);
+            eot_beta(M, b, n, m, eta, alpha, beta);
+            double sh = beta[k1];
+            for (int j = 0; j < m; ++j) beta[j] -= sh;
+            eot_eval_T(M, a, n, m, eta, beta, T, c);
+        }
+        ++it;
+    }
+    for (int j = 0; j < m; ++j) beta_out[j] = beta[j];
+    return conv ? it : -1;
+}
+
+/* eq (13): D = d<G, T*>/dM =
+ *   eta^-1 [diag((mu_r - T*_{-m} w_{-m}) / a) T* + T* diag(w) - G o T*],
+ *   w_{-m} = Delta^-1 [mu_c - (T*_{-m})^T (mu_r / a)],  w_m = 0,
+ *   mu_r = (G o T*) 1_m,  mu_c = (G o T*)^T_{-m} 1_n,
+ *   Delta = diag(b_{-m}) - (T*)^T_{-m} diag(a)^-1 T*_{-m}.
+ * Returns -1 when Delta is singular (D is then NaN). */
+static int eot_bwd_one(const double *T, const double *G, const double *a, const double *b, int n, int m,
+                       double eta, double *D)
+{
+    const int k1 = m - 1;
+    double gam[ORACLE_NMAX * ORACLE_NMAX], mur[ORACLE_NMAX], rhs[ORACLE_NMAX];
+    double delta[ORACLE_NMAX * ORACLE_NMAX], w[ORACLE_NMAX], v[ORACLE_NMAX];
+    for (int k = 0; k < n * m; ++k) gam[k] = G[k] * T[k];
+    for (int i = 0; i < n; ++i) {
+        double s = 0.0;
+        for (int j = 0; j < m; ++j) s += gam[i * m + j];
+        mur[i] = s;
+    }
+    for (int j = 0; j < k1; ++j) {
+        double mc = 0.0, tm = 0.0;
+        for (int i = 0; i < n; ++i) {
+            mc += gam[i * m + j];
+            tm += T[i * m + j] * mur[i] / a[i];
+        }
+        rhs[j] = mc - tm;
+        for (int k = 0; k < k1; ++k) {
+            double p = 0.0;
+            for (int i = 0; i < n; ++i) p += T[i * m + j] / a[i] * T[i * m + k];
+            delta[j * k1 + k] = (j == k ? b[j] : 0.0) - p;
+        }
+    }
+    int rc = solve_gepp(delta, rhs, k1);
+    for (int j = 0; j < k1; ++j) w[j] = rc == 0 ? rhs[j] : NAN;
+    w[k1] = 0.0;
+    for (int i = 0; i < n; ++i) {
+        double s = mur[i];
+        for (int j = 0; j < k1; ++j) s -= T[i * m + j] * w[j];
+        v[i] = s;
+    }
+    for (int i = 0; i < n; ++i)
+        for (int j = 0; j < m; ++j)
+            D[i * m + j] = (v[i] / a[i] * T[i * m + j] + T[i * m + j] * w[j] - gam[i * m + j]) / eta;
+    return rc;
+}
+
+/* ------------------------------------------------------------------ */
 /* exported entry points                                                */
 /* ------------------------------------------------------------------ */
 
@@ -483,5 +721,94 @@ int oracle_residuals(const double *T, int64_t B, int n, double *res)
     if (bad_args(B, n, T) || (B > 0 && !res)) return -1;
 #pragma omp parallel for schedule(static)
     for (int64_t b = 0; b < B; ++b) res[b] = marginal_residual(T + b * n * n, n);
+    return 0;
+}
+
+/* ---- general entropic OT: a [B, n], b [B, m], M / T / G / D [B, n, m] ---- */
+
+static int eot_bad_args(int64_t B, int n, int m, double eta, const void *p)
+{
+    return B < 0 || n < 1 || m < 2 || n > ORACLE_NMAX || m > ORACLE_NMAX || !(eta > 0.0) || (B > 0 && p == NULL);
+}
+
+int oracle_eot_sinkhorn_tol(const double *M, const double *a, const double *b, int64_t B, int n, int m, double eta,
+                            double tol, int cap, double *T, double *beta, int32_t *sweeps, int32_t *converged)
+{
+    if (eot_bad_args(B, n, m, eta, M) || (B > 0 && (!a || !b || !T || !beta || !sweeps || !converged)) || cap < 0)
+        return -1;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t q = 0; q < B; ++q) {
+        int conv = 0;
+        sweeps[q] = eot_sk_one(M + q * n * m, a + q * n, b + q * m, n, m, eta, tol, cap, T + q * n * m,
+                               beta + q * m, &conv);
+        converged[q] = conv;
+    }
+    return 0;
+}
+
+int oracle_eot_newton(const double *M, const double *a, const double *b, int64_t B, int n, int m, double eta,
+                      double tol, int max_iter, double *T, double *beta, int32_t *iters)
+{
+    if (eot_bad_args(B, n, m, eta, M) || (B > 0 && (!a || !b || !T || !beta || !iters)) || max_iter < 0) return -1;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t q = 0; q < B; ++q)
+        iters[q] = eot_newton_one(M + q * n * m, a + q * n, b + q * m, n, m, eta, tol, max_iter, T + q * n * m,
+                                  beta + q * m);
+    return 0;
+}
+
+/* Reference plan, certified as in oracle_project (Sinkhorn to 1e-13 and an
+ * independent Newton, or Newton plus a Sinkhorn fixed-point check). */
+int oracle_eot_project(const double *M, const double *a, const double *b, int64_t B, int n, int m, double eta,
+                       int sk_cap, double *T, double *beta, int32_t *status)
+{
+    if (eot_bad_args(B, n, m, eta, M) || (B > 0 && (!a || !b || !T || !beta || !status)) || sk_cap < 0) return -1;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t q = 0; q < B; ++q) {
+        const double *Mq = M + q * n * m, *aq = a + q * n, *bq = b + q * m;
+        double tsk[ORACLE_NMAX * ORACLE_NMAX], tnw[ORACLE_NMAX * ORACLE_NMAX];
+        double bsk[ORACLE_NMAX], bnw[ORACLE_NMAX];
+        int conv = 0;
+        eot_sk_one(Mq, aq, bq, n, m, eta, 1e-13, sk_cap, tsk, bsk, &conv);
+        int it = eot_newton_one(Mq, aq, bq, n, m, eta, 1e-13, 500, tnw, bnw);
+        int st;
+        if (conv) {
+            st = (it >= 0 && max_abs_diff(tsk, tnw, n * m) <= 1e-12) ? 0 : -1;
+            memcpy(T + q * n * m, tsk, sizeof(double) * n * m);
+            memcpy(beta + q * m, bsk, sizeof(double) * m);
+        } else {
+            st = -2;
+            if (it >= 0) {
+                double alpha[ORACLE_NMAX], b1[ORACLE_NMAX], t1[ORACLE_NMAX * ORACLE_NMAX];
+                eot_alpha(Mq, aq, n, m, eta, bnw, alpha);
+                eot_beta(Mq, bq, n, m, eta, alpha, b1);
+                eot_primal(Mq, n, m, eta, alpha, b1, t1);
+                if (max_abs_diff(t1, tnw, n * m) <= 1e-12) st = 1;
+            }
+            memcpy(T + q * n * m, tnw, sizeof(double) * n * m);
+            memcpy(beta + q * m, bnw, sizeof(double) * m);
+        }
+        status[q] = st;
+    }
+    return 0;
+}
+
+/* eq (13) at the given plans; returns the number of singular Delta, or -1. */
+int oracle_eot_bwd(const double *T, const double *G, const double *a, const double *b, int64_t B, int n, int m,
+                   double eta, double *D)
+{
+    if (eot_bad_args(B, n, m, eta, T) || (B > 0 && (!G || !a || !b || !D))) return -1;
+    int64_t bad = 0;
+#pragma omp parallel for schedule(static) reduction(+ : bad)
+    for (int64_t q = 0; q < B; ++q)
+        if (eot_bwd_one(T + q * n * m, G + q * n * m, a + q * n, b + q * m, n, m, eta, D + q * n * m) != 0) ++bad;
+    return (int)(bad > 0x7fffffff ? 0x7fffffff : bad);
+}
+
+int oracle_eot_residuals(const double *T, const double *a, const double *b, int64_t B, int n, int m, double *res)
+{
+    if (eot_bad_args(B, n, m, 1.0, T) || (B > 0 && (!a || !b || !res))) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t q = 0; q < B; ++q) res[q] = eot_marginal_residual(T + q * n * m, a + q * n, b + q * m, n, m);
     return 0;
 }

@@ -1,7 +1,9 @@
 """Plant plausible slips in a copy of the oracle (on the CPU) and check that the
 pins in test_oracle.py catch every one of them.
 
-Each mutant is oracle.c with one textual edit (a flipped sign, a dropped term,
+Both pin files (test_oracle.py for the Birkhoff functions, test_oracle_eot.py
+for the general entropic OT) run against every mutant.  Each mutant is oracle.c
+with one textual edit (a flipped sign, a dropped term,
 a transposed index, a lost gauge), compiled to a temporary library and loaded
 by the oracle's Python wrapper through ORACLE_LIB in a child pytest run.
 """
@@ -34,6 +36,30 @@ MUTANTS = {
     "gradient_sign": ("g[j] = c[j] - 1.0; gn2 += g[j] * g[j];", "g[j] = 1.0 - c[j]; gn2 += g[j] * g[j];"),
     "linesearch_df_sign": ("for (int j = 0; j < m; ++j) df -= gam * d[j];", "for (int j = 0; j < m; ++j) df += gam * d[j];"),
     "softmax_no_max_shift_wrong": ("double e = exp(H[i * n + j] + beta[j] - mu);", "double e = exp(H[i * n + j] - beta[j] - mu);"),
+    # general entropic OT (cost M, marginals a and b, eta)
+    "eot_alpha_drop_loga": ("alpha[i] = eta * log(a[i]) - eta * lse(u, m, 1);", "alpha[i] = -eta * lse(u, m, 1);"),
+    "eot_beta_sign": ("beta[j] = eta * log(b[j]) - eta * lse(u, n, 1);", "beta[j] = eta * log(b[j]) + eta * lse(u, n, 1);"),
+    "eot_alpha_drop_eta": ("for (int j = 0; j < m; ++j) u[j] = (beta[j] - M[i * m + j]) / eta;",
+                           "for (int j = 0; j < m; ++j) u[j] = (beta[j] - M[i * m + j]);"),
+    "eot_primal_beta_sign": ("exp((alpha[i] + beta[j] - M[i * m + j]) / eta)", "exp((alpha[i] - beta[j] - M[i * m + j]) / eta)"),
+    "eot_sk_lost_gauge": ("for (int j = 0; j < m; ++j) beta_out[j] = beta[j] - beta[m - 1];",
+                          "for (int j = 0; j < m; ++j) beta_out[j] = beta[j];"),
+    "eot_plan_drop_a": ("for (int j = 0; j < m; ++j) T[i * m + j] *= a[i] / s;", "for (int j = 0; j < m; ++j) T[i * m + j] *= 1.0 / s;"),
+    "eot_hessian_drop_inv_a": ("for (int i = 0; i < n; ++i) p += T[i * m + j] * T[i * m + k] / a[i];",
+                               "for (int i = 0; i < n; ++i) p += T[i * m + j] * T[i * m + k];"),
+    "eot_hessian_drop_eta": ("hess[j * k1 + k] = ((j == k ? c[j] : 0.0) - p) / eta;", "hess[j * k1 + k] = ((j == k ? c[j] : 0.0) - p);"),
+    "eot_gradient_marginal": ("for (int j = 0; j < k1; ++j) { g[j] = c[j] - b[j]; gn2 += g[j] * g[j]; }",
+                              "for (int j = 0; j < k1; ++j) { g[j] = c[j] - 1.0 / m; gn2 += g[j] * g[j]; }"),
+    "eot_df_drop_eta": ("df += eta * a[i] * log1p(acc);", "df += a[i] * log1p(acc);"),
+    "eot_df_expm1_eta": ("acc += T[i * m + j] / a[i] * expm1(gam * d[j] / eta);", "acc += T[i * m + j] / a[i] * expm1(gam * d[j]);"),
+    "eot_bwd_drop_inv_a": ("(v[i] / a[i] * T[i * m + j] + T[i * m + j] * w[j] - gam[i * m + j]) / eta",
+                           "(v[i] * T[i * m + j] + T[i * m + j] * w[j] - gam[i * m + j]) / eta"),
+    "eot_bwd_drop_eta": ("(v[i] / a[i] * T[i * m + j] + T[i * m + j] * w[j] - gam[i * m + j]) / eta",
+                         "(v[i] / a[i] * T[i * m + j] + T[i * m + j] * w[j] - gam[i * m + j])"),
+    "eot_bwd_delta_b": ("delta[j * k1 + k] = (j == k ? b[j] : 0.0) - p;", "delta[j * k1 + k] = (j == k ? 1.0 : 0.0) - p;"),
+    "eot_bwd_rhs_drop_inv_a": ("tm += T[i * m + j] * mur[i] / a[i];", "tm += T[i * m + j] * mur[i];"),
+    "eot_bwd_delta_drop_inv_a": ("for (int i = 0; i < n; ++i) p += T[i * m + j] / a[i] * T[i * m + k];",
+                                 "for (int i = 0; i < n; ++i) p += T[i * m + j] * T[i * m + k];"),
 }
 
 
@@ -47,7 +73,7 @@ def _run_mutant(name, tmp):
                    check=True)
     env = dict(os.environ, ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        str(ROOT / "tests" / "test_oracle.py")],
+                        str(ROOT / "tests" / "test_oracle.py"), str(ROOT / "tests" / "test_oracle_eot.py")],
                        cwd=str(ROOT), env=env, capture_output=True, text=True, timeout=600)
     return name, r.returncode, r.stdout[-400:]
 
