@@ -22,8 +22,10 @@ __all__ = [
     "BirkhoffError", "library_path", "load_library",
     "birkhoff_fwd", "birkhoff_fwd_ex", "birkhoff_bwd", "birkhoff_bwd_from_T", "sinkhorn_fwd",
     "birkhoff_fwd_bf16", "birkhoff_bwd_bf16", "birkhoff_fwd_bwd", "birkhoff_fwd_bwd_bf16",
+    "birkhoff_eot_fwd", "birkhoff_eot_bwd",
     "birkhoff_strerror", "birkhoff_abi_version",
     "project", "project_bwd", "project_fwd_bwd", "sinkhorn", "BirkhoffProjection",
+    "eot_plan", "eot_plan_bwd", "EntropicOT",
 ]
 
 _PKG = pathlib.Path(__file__).resolve().parent
@@ -63,6 +65,8 @@ def load_library():
         "birkhoff_bwd_bf16": [vp, vp, vp, vp, i64, ci, vp],
         "birkhoff_fwd_bwd": [vp, vp, vp, vp, vp, i64, ci, cf, ci, vp],
         "birkhoff_fwd_bwd_bf16": [vp, vp, vp, vp, vp, i64, ci, cf, ci, vp],
+        "birkhoff_eot_fwd": [vp, vp, vp, ci, vp, vp, vp, i64, ci, ci, cf, cf, ci, vp],
+        "birkhoff_eot_bwd": [vp, vp, vp, ci, vp, i64, ci, ci, cf, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -264,6 +268,65 @@ def birkhoff_fwd_bwd_bf16(logits, dT, T, dual, dH, tol: float = 1e-6, max_iter: 
           int(max_iter), _stream_handle(stream, dev))
 
 
+def _plans(x, name, B=None, n=None, m=None):
+    torch = _torch()
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not x.is_cuda or x.dtype != torch.float32 or not x.is_contiguous():
+        raise ValueError("%s must be a contiguous float32 GPU tensor" % name)
+    if x.dim() != 3:
+        raise ValueError("%s must have shape [B, n, m], got %s" % (name, tuple(x.shape)))
+    if B is not None and tuple(x.shape) != (B, n, m):
+        raise ValueError("%s must have shape %s, got %s" % (name, (B, n, m), tuple(x.shape)))
+    return x
+
+
+def _marginal(x, name, B, k):
+    """A marginal is [B, k] (one per problem) or [k] (shared); returns the shared flag."""
+    torch = _torch()
+    if not isinstance(x, torch.Tensor) or not x.is_cuda or x.dtype != torch.float32 or not x.is_contiguous():
+        raise ValueError("%s must be a contiguous float32 GPU tensor" % name)
+    if tuple(x.shape) == (k,):
+        return 1
+    if tuple(x.shape) == (B, k):
+        return 0
+    raise ValueError("%s must have shape [%d] or [%d, %d], got %s" % (name, k, B, k, tuple(x.shape)))
+
+
+def birkhoff_eot_fwd(cost, a, b, T, dual, iters=None, eta: float = 1.0, tol: float = 1e-6, max_iter: int = 50,
+                     stream=None) -> None:
+    """General entropic OT plan: cost [B,n,m], marginals a ([B,n] or [n]) and b ([B,m] or [m]);
+    writes T [B,n,m], dual [B,m] and optionally iters [B] int32."""
+    torch = _torch()
+    _plans(cost, "cost")
+    B, n, m = cost.shape
+    sa, sb = _marginal(a, "a", B, n), _marginal(b, "b", B, m)
+    if sa != sb:
+        raise ValueError("a and b must both be shared or both be per problem")
+    _plans(T, "T", B, n, m)
+    _vec(dual, "dual", B, m, torch.float32)
+    ts = [cost, a, b, T, dual]
+    if iters is not None:
+        _vec(iters, "iters", B, None, torch.int32)
+        ts.append(iters)
+    dev = _same_device(*ts)
+    _call("birkhoff_eot_fwd", dev, _p(cost), _p(a), _p(b), sa, _p(T), _p(dual),
+          _p(iters) if iters is not None else None, B, n, m, float(eta), float(tol), int(max_iter),
+          _stream_handle(stream, dev))
+
+
+def birkhoff_eot_bwd(T, dT, a, dcost, eta: float = 1.0, stream=None) -> None:
+    """eq (13) for the general problem: dcost = dL/dcost from the plan T and dT = dL/dT."""
+    _plans(T, "T")
+    B, n, m = T.shape
+    sa = _marginal(a, "a", B, n)
+    _plans(dT, "dT", B, n, m)
+    _plans(dcost, "dcost", B, n, m)
+    dev = _same_device(T, dT, a, dcost)
+    _call("birkhoff_eot_bwd", dev, _p(T), _p(dT), _p(a), sa, _p(dcost), B, n, m, float(eta),
+          _stream_handle(stream, dev))
+
+
 # ------------------------------------------------------- allocating helpers
 
 def project(logits, tol: float = 1e-6, max_iter: int = 50, stream=None):
@@ -310,6 +373,25 @@ def sinkhorn(logits, iters: int = 20, stream=None):
     return T
 
 
+def eot_plan(cost, a, b, eta: float = 1.0, tol: float = 1e-6, max_iter: int = 50, with_iters: bool = False,
+             stream=None):
+    """Allocate outputs and solve the general problems. Returns (T, dual) or (T, dual, iters)."""
+    torch = _torch()
+    B, n, m = cost.shape
+    T = torch.empty((B, n, m), dtype=torch.float32, device=cost.device)
+    dual = torch.empty((B, m), dtype=torch.float32, device=cost.device)
+    iters = torch.empty((B,), dtype=torch.int32, device=cost.device) if with_iters else None
+    birkhoff_eot_fwd(cost, a, b, T, dual, iters, eta, tol, max_iter, stream)
+    return (T, dual, iters) if with_iters else (T, dual)
+
+
+def eot_plan_bwd(T, dT, a, eta: float = 1.0, stream=None):
+    """Allocate dcost and run eq (13)."""
+    dcost = _torch().empty_like(T)
+    birkhoff_eot_bwd(T, dT, a, dcost, eta, stream)
+    return dcost
+
+
 def _autograd_function():
     torch = _torch()
 
@@ -331,16 +413,36 @@ def _autograd_function():
             logits, dual = ctx.saved_tensors
             return project_bwd(logits, dual, dT.contiguous()), None, None
 
-    return BirkhoffProjection
+    class EntropicOT(torch.autograd.Function):
+        """Plan of the entropic OT problem with cost `cost` and fixed marginals a, b,
+        differentiable in the cost by eq (13).  Saves (T, a)."""
+
+        @staticmethod
+        def forward(ctx, cost, a, b, eta: float = 1.0, tol: float = 1e-6, max_iter: int = 50):
+            T, _ = eot_plan(cost.contiguous(), a, b, eta, tol, max_iter)
+            ctx.save_for_backward(T, a)
+            ctx.eta = eta
+            return T
+
+        @staticmethod
+        def backward(ctx, dT):
+            T, a = ctx.saved_tensors
+            return eot_plan_bwd(T, dT.contiguous(), a, ctx.eta), None, None, None, None, None
+
+    return {"BirkhoffProjection": BirkhoffProjection, "EntropicOT": EntropicOT}
 
 
 class _LazyFunction:
-    _fn = None
+    _fns = None
+
+    def __init__(self, name):
+        self._name = name
 
     def __getattr__(self, item):
-        if _LazyFunction._fn is None:
-            _LazyFunction._fn = _autograd_function()
-        return getattr(_LazyFunction._fn, item)
+        if _LazyFunction._fns is None:
+            _LazyFunction._fns = _autograd_function()
+        return getattr(_LazyFunction._fns[self._name], item)
 
 
-BirkhoffProjection = _LazyFunction()
+BirkhoffProjection = _LazyFunction("BirkhoffProjection")
+EntropicOT = _LazyFunction("EntropicOT")

@@ -18,7 +18,7 @@ PKG = pathlib.Path(__file__).resolve().parent
 ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libbirkhoff.so"
-SOURCES = [CSRC / "birkhoff.hip"]
+SOURCES = sorted(CSRC.glob("*.hip"))
 ARCH = "gfx950"
 
 
@@ -41,28 +41,52 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libbirkhoff)")
 
 
-def command(out: pathlib.Path, resource_usage: bool = False) -> list:
-    cmd = [hipcc(), "--offload-arch=%s" % ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-Wall", "-I", str(ROOT / "include"), "-I", str(CSRC)]
+def flags(resource_usage: bool = False) -> list:
+    f = ["--offload-arch=%s" % ARCH, "-O3", "-std=c++17", "-fPIC",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wall", "-I", str(ROOT / "include"), "-I", str(CSRC)]
     if resource_usage:
-        cmd += ["-Rpass-analysis=kernel-resource-usage"]
-    cmd += [str(s) for s in SOURCES] + ["-o", str(out)]
-    return cmd
+        f += ["-Rpass-analysis=kernel-resource-usage"]
+    return f
+
+
+# the host pass does not know the packed-fp32 target feature and says so
+_NOISE = "is not a recognized feature for this target"
+
+
+def _errors(stderr: str) -> str:
+    return "\n".join(l for l in stderr.splitlines() if _NOISE not in l)
 
 
 def build(resource_usage: bool = False, quiet: bool = True) -> pathlib.Path:
-    """Compile every HIP source into libbirkhoff.so (always recompiles)."""
-    tmp = LIB.with_suffix(".so.tmp%d" % os.getpid())
-    r = subprocess.run(command(tmp, resource_usage), capture_output=True, text=True)
-    # the host pass does not know the packed-fp32 target feature and says so; drop that line
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + err)
-    if err.strip() and not quiet:
-        print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
+    """Compile every HIP source into libbirkhoff.so (always recompiles).  The
+    translation units are compiled in parallel, then linked."""
+    tag = "tmp%d" % os.getpid()
+    objs = [LIB.with_name("%s.%s.o" % (src.stem, tag)) for src in SOURCES]
+    procs = [subprocess.Popen([hipcc()] + flags(resource_usage) + ["-c", str(src), "-o", str(obj)],
+                              stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+             for src, obj in zip(SOURCES, objs)]
+    errs, failed = [], False
+    for pr in procs:
+        _, err = pr.communicate()
+        failed |= pr.returncode != 0
+        errs.append(_errors(err))
+    tmp = LIB.with_suffix(".so." + tag)
+    try:
+        if failed:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(errs))
+        r = subprocess.run([hipcc(), "--offload-arch=%s" % ARCH, "-shared", "-fPIC"] + [str(o) for o in objs]
+                           + ["-o", str(tmp)], capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("hipcc link failed:\n" + _errors(r.stderr))
+        err = "\n".join(errs + [_errors(r.stderr)]).strip()
+        if err and not quiet:
+            print(err, file=sys.stderr)
+        os.replace(tmp, LIB)
+    finally:
+        for o in objs + [tmp]:
+            if o.exists():
+                o.unlink()
     return LIB
 
 

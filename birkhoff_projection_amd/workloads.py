@@ -13,6 +13,13 @@ row-major and stored back to back, shape [B, n, n].
 The distributions follow the pages' experiments ("Accelerating Birkhoff
 Projection for Manifold-Constrained Hyper-Connections", section 5: N(0,1),
 N(0,10^2)) and the benchmark shapes below; no dataset is involved.
+
+General entropic OT workloads (EOT_WORKLOADS, the problem of section 2.3 with
+a cost, marginals and eta): costs are drawn like logits (seed), the upstream
+dL/dT from seed + 100, and the marginals from seed + 200 as dyadic
+rationals k / 2^20 (k integers summing to 2^20), so that a and b are exact in
+fp32, sum to exactly 1 in any precision, and the problem has an exact
+solution whether it is read in fp32 or float64.
 """
 from __future__ import annotations
 
@@ -65,29 +72,30 @@ WORKLOADS = {
 }
 
 
-def _draw(recipe: Tuple, B: int, n: int, seed: int) -> np.ndarray:
-    """fp32 [B, n, n] values for a recipe (scaling done in float64, then rounded)."""
+def _draw(recipe: Tuple, B: int, n: int, seed: int, m: Optional[int] = None) -> np.ndarray:
+    """fp32 [B, n, m] (m defaults to n) values for a recipe (scaling done in float64, then rounded)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     kind = recipe[0]
-    out = np.empty((B, n, n), dtype=np.float32)
+    m = n if m is None else int(m)
+    out = np.empty((B, n, m), dtype=np.float32)
     if kind == "normal":
         sigma = float(recipe[1])
         for s in range(0, B, _CHUNK):
             e = min(B, s + _CHUNK)
-            out[s:e] = sigma * rng.standard_normal((e - s, n, n))
+            out[s:e] = sigma * rng.standard_normal((e - s, n, m))
     elif kind == "sigma_mix":
         sigmas = np.asarray(recipe[1], dtype=np.float64)
         idx = rng.integers(0, len(sigmas), size=B)          # sigma index first
         for s in range(0, B, _CHUNK):
             e = min(B, s + _CHUNK)
-            z = rng.standard_normal((e - s, n, n))
+            z = rng.standard_normal((e - s, n, m))
             out[s:e] = sigmas[idx[s:e]][:, None, None] * z
     elif kind == "near_identity":
         sigma, diag = float(recipe[1]), float(recipe[2])
-        eye = np.eye(n) * diag
+        eye = np.eye(n, m) * diag
         for s in range(0, B, _CHUNK):
             e = min(B, s + _CHUNK)
-            out[s:e] = sigma * rng.standard_normal((e - s, n, n)) + eye
+            out[s:e] = sigma * rng.standard_normal((e - s, n, m)) + eye
     else:
         raise ValueError("unknown recipe %r" % (kind,))
     return out
@@ -149,6 +157,83 @@ def bytes_per_projection(n: int, io: str, passes: str) -> int:
         return bwd
     if passes == "fused":
         return 4 * n * n * s + 4 * n
+    if passes == "fwd+bwd":
+        return fwd + bwd
+    raise ValueError("unknown passes %r" % (passes,))
+
+
+# ---------------------------------------------------------------------------
+# General small entropic OT (cost M, marginals a and b, eta)
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class EotWorkload:
+    key: str
+    title: str
+    B: int
+    n: int
+    m: int
+    eta: float                   # exactly representable in fp32
+    cost: Tuple                  # recipe for M, as for logits
+    marginals: Tuple             # ("dyadic", lo, hi): weights ~ U(lo, hi), see make_marginals
+    upstream: Tuple              # recipe for dL/dT
+    seed: int
+    shared: bool = False         # one (a, b) pair for the whole batch
+    tol: float = 1e-6
+    max_iter: int = 50
+    sk_cap: int = 10_000
+
+
+EOT_WORKLOADS = {
+    "eot": EotWorkload(
+        key="eot", title="4x6 fp32 entropic OT, B=1,048,576, M~N(0,1), eta=1/2, per-problem marginals "
+                         "~U(0.5,1.5) normalised, dT~N(0,1)",
+        B=1 << 20, n=4, m=6, eta=0.5, cost=("normal", 1.0), marginals=("dyadic", 0.5, 1.5),
+        upstream=("normal", 1.0), seed=6),
+}
+
+
+def make_marginals(recipe: Tuple, B: int, k: int, seed: int) -> np.ndarray:
+    """fp32 [B, k] marginals: weights w ~ U(lo, hi) in float64, turned into integers
+    q = floor(w / sum(w) * 2^20) whose shortfall from 2^20 is added to the largest,
+    then a = q / 2^20 (exact in fp32; every row sums to exactly 1)."""
+    kind, lo, hi = recipe
+    if kind != "dyadic":
+        raise ValueError("unknown marginal recipe %r" % (kind,))
+    rng = np.random.Generator(np.random.PCG64(seed))
+    w = rng.uniform(lo, hi, size=(B, k))
+    q = np.floor(w / w.sum(1, keepdims=True) * (1 << 20)).astype(np.int64)
+    q[np.arange(B), q.argmax(1)] += (1 << 20) - q.sum(1)
+    return (q / float(1 << 20)).astype(np.float32)
+
+
+def make_eot(w: EotWorkload, B: Optional[int] = None, seed: Optional[int] = None):
+    """(cost [B, n, m], a, b) fp32 for workload w; a, b are [B, n], [B, m], or [n], [m] when shared."""
+    B = w.B if B is None else int(B)
+    sd = w.seed if seed is None else seed
+    M = _draw(w.cost, B, w.n, sd, w.m)
+    nb = 1 if w.shared else B
+    a = make_marginals(w.marginals, nb, w.n, sd + 200)
+    b = make_marginals(w.marginals, nb, w.m, sd + 300)
+    return (M, a[0], b[0]) if w.shared else (M, a, b)
+
+
+def make_eot_upstream(w: EotWorkload, B: Optional[int] = None, seed: Optional[int] = None) -> np.ndarray:
+    B = w.B if B is None else int(B)
+    return _draw(w.upstream, B, w.n, (w.seed + 100) if seed is None else seed, w.m)
+
+
+def eot_bytes_per_problem(n: int, m: int, passes: str, shared: bool) -> int:
+    """Algorithmic HBM bytes per problem (fp32), each input read once, each output written once.
+
+    fwd: cost + T (n*m each) + dual (m) + the marginals (n + m) unless shared;
+    bwd: T + dT + dcost (n*m each) + a (n) unless shared."""
+    fwd = 4 * (2 * n * m + m + (0 if shared else n + m))
+    bwd = 4 * (3 * n * m + (0 if shared else n))
+    if passes == "fwd":
+        return fwd
+    if passes == "bwd":
+        return bwd
     if passes == "fwd+bwd":
         return fwd + bwd
     raise ValueError("unknown passes %r" % (passes,))

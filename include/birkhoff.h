@@ -125,6 +125,53 @@ int birkhoff_fwd_bwd(const float* logits, const float* dT, float* T, float* dual
 int birkhoff_fwd_bwd_bf16(const uint16_t* logits, const uint16_t* dT, uint16_t* T, float* dual, uint16_t* dH,
                           int64_t B, int n, float tol, int max_iter, void* stream);
 
+/* ---- General small entropic optimal transport ------------------------------
+ * For every one of B independent problems with cost M (n x m), marginals
+ * a > 0 (n) and b > 0 (m) with sum(a) = sum(b), and regularisation eta > 0,
+ * the forward pass returns the plan
+ *
+ *     T = argmin { <T, M> - eta h(T) : T 1 = a, T^T 1 = b }      (section 2.3, eq (3)),
+ *
+ * T_ij = exp((alpha_i + beta_j - M_ij) / eta) at the optimal dual (eq (4)).  It is
+ * found by Newton's method on the reduced dual of eq (8) with the gradient and
+ * Hessian of eq (9), with the same step-size rule and Sinkhorn fallback (eqs
+ * (5)-(7)) as the Birkhoff forward; the backward pass is eq (13) (section 4.1).
+ * The Birkhoff projection is the case a = b = 1, eta = 1, M = -H.
+ *
+ * Shapes: 1 <= n <= 8 rows, 2 <= m <= 8 columns.  Layouts as above: cost, T, dT
+ * and dcost are [B, n, m] row-major back to back; the dual is [B, m].  With
+ * shared_marginals == 0, a is [B, n] and b is [B, m] (one pair per problem);
+ * with shared_marginals != 0, a is [n] and b is [m], used by every problem
+ * (these two need only 4-byte alignment).  Marginals are not checked for
+ * positivity or equal sums: a problem whose marginals violate this has no
+ * plan, and its outputs are whatever the iteration reached (its iters entry
+ * is -1 unless the column residual happens to fall below tol).
+ * Return codes as above; BIRKHOFF_EINVAL also covers n or m out of range and
+ * eta <= 0 or not finite. */
+
+/* Forward pass (fp32).
+ *   cost     [B, n, m] input M;  a, b marginals (see shared_marginals)
+ *   T        [B, n, m] output plan (rows sum to a up to rounding)
+ *   dual     [B, m] output beta in cost units with beta_{m-1} = 0, such that
+ *            T_ij = a_i exp((beta_j - M_ij) / eta) / sum_k exp((beta_k - M_ik) / eta)
+ *            (section 3.1)
+ *   iters    [B] int32 output or NULL: updates taken, -1 when tol was not reached
+ *   tol      stop when every column sum of T is within tol of b_j (absolute)
+ *   max_iter cap on updates (accepted steps or fallback sweeps), >= 1 */
+int birkhoff_eot_fwd(const float* cost, const float* a, const float* b, int shared_marginals, float* T, float* dual,
+                     int32_t* iters, int64_t B, int n, int m, float eta, float tol, int max_iter, void* stream);
+
+/* Backward pass (fp32), eq (13): dcost = dL/dM from the plan and dL/dT.
+ *   T      [B, n, m] a plan (e.g. birkhoff_eot_fwd's output)
+ *   dT     [B, n, m] upstream gradient dL/dT
+ *   a      row marginals (see shared_marginals); b is not needed: eq (13)'s Delta
+ *          is recomputed from T as the Hessian of eq (9) at T (section 4.2),
+ *          which equals diag(b_{-m}) - T_{-m}^T diag(a)^-1 T_{-m} at the optimum
+ *   dcost  [B, n, m] output dL/dM
+ * No argument may alias another. */
+int birkhoff_eot_bwd(const float* T, const float* dT, const float* a, int shared_marginals, float* dcost, int64_t B,
+                     int n, int m, float eta, void* stream);
+
 /* Static description of a return code (never NULL). */
 const char* birkhoff_strerror(int code);
 

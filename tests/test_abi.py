@@ -33,7 +33,7 @@ def test_header_declares_the_entry_points():
     names = declared_symbols()
     for n in ("birkhoff_fwd", "birkhoff_fwd_ex", "birkhoff_bwd", "sinkhorn_fwd",
               "birkhoff_fwd_bf16", "birkhoff_bwd_bf16", "birkhoff_fwd_bwd", "birkhoff_fwd_bwd_bf16",
-              "birkhoff_bwd_from_T",
+              "birkhoff_bwd_from_T", "birkhoff_eot_fwd", "birkhoff_eot_bwd",
               "birkhoff_strerror", "birkhoff_abi_version"):
         assert n in names
 
@@ -142,6 +142,67 @@ def test_backward_and_sinkhorn_argument_checks(lib):
     assert lib.sinkhorn_fwd(P[0], P[1], 5, 4, -3, None) == EINVAL
     assert lib.sinkhorn_fwd(P[0], P[1], 5, 7, 20, None) == EINVAL
     assert lib.sinkhorn_fwd(None, None, 0, 4, 20, None) == 0
+
+
+# birkhoff_eot_fwd(cost, a, b, shared, T, dual, iters, B, n, m, eta, tol, max_iter, stream)
+@pytest.mark.parametrize("B,n,m,eta,tol,it,want", [
+    (-1, 4, 6, 0.5, 1e-6, 50, EINVAL),
+    (5, 0, 6, 0.5, 1e-6, 50, EINVAL),
+    (5, 9, 6, 0.5, 1e-6, 50, EINVAL),
+    (5, 4, 1, 0.5, 1e-6, 50, EINVAL),
+    (5, 4, 9, 0.5, 1e-6, 50, EINVAL),
+    (5, 4, 6, 0.0, 1e-6, 50, EINVAL),
+    (5, 4, 6, -1.0, 1e-6, 50, EINVAL),
+    (5, 4, 6, math.nan, 1e-6, 50, EINVAL),
+    (5, 4, 6, math.inf, 1e-6, 50, EINVAL),
+    (5, 4, 6, 0.5, 0.0, 50, EINVAL),
+    (5, 4, 6, 0.5, math.nan, 50, EINVAL),
+    (5, 4, 6, 0.5, 1e-6, 0, EINVAL),
+    (1 << 50, 4, 6, 0.5, 1e-6, 50, EINVAL),
+    (0, 1, 2, 0.5, 1e-6, 50, 0),
+    (0, 8, 8, 0.5, 1e-6, 50, 0),
+])
+def test_eot_forward_argument_checks(lib, B, n, m, eta, tol, it, want):
+    Q = [A, A + 4096, A + 8192, A + 12288, A + 16384, A + 20480]
+    for shared in (0, 1):
+        assert lib.birkhoff_eot_fwd(Q[0], Q[1], Q[2], shared, Q[3], Q[4], Q[5], B, n, m, eta, tol, it, None) == want
+        assert lib.birkhoff_eot_fwd(Q[0], Q[1], Q[2], shared, Q[3], Q[4], None, B, n, m, eta, tol, it, None) == want
+
+
+def test_eot_null_and_misaligned_pointers(lib):
+    """Every call here is rejected on the host (none may reach a launch: the
+    addresses are fake)."""
+    Q = [A, A + 4096, A + 8192, A + 12288, A + 16384]   # cost, a, b, T, dual
+
+    def call(p, shared, iters=None):
+        return lib.birkhoff_eot_fwd(p[0], p[1], p[2], shared, p[3], p[4], iters, 9, 3, 5, 0.5, 1e-6, 50, None)
+
+    for k in range(5):
+        for shared in (0, 1):
+            ptrs = list(Q)
+            ptrs[k] = None
+            assert call(ptrs, shared) == EINVAL
+            # per-problem marginals and the matrices need 16 bytes, shared marginals 4
+            ptrs[k] = Q[k] + (2 if (shared and k in (1, 2)) else 4)
+            assert call(ptrs, shared) == EALIGN
+    assert call(Q, 0, iters=A + 24578) == EALIGN
+
+
+def test_eot_backward_argument_checks(lib):
+    # birkhoff_eot_bwd(T, dT, a, shared, dcost, B, n, m, eta, stream)
+    Q = [A, A + 4096, A + 8192, A + 12288]
+    assert lib.birkhoff_eot_bwd(Q[0], Q[1], Q[2], 0, Q[3], -1, 4, 6, 0.5, None) == EINVAL
+    assert lib.birkhoff_eot_bwd(Q[0], Q[1], Q[2], 0, Q[3], 5, 4, 1, 0.5, None) == EINVAL
+    assert lib.birkhoff_eot_bwd(Q[0], Q[1], Q[2], 0, Q[3], 5, 9, 6, 0.5, None) == EINVAL
+    assert lib.birkhoff_eot_bwd(Q[0], Q[1], Q[2], 0, Q[3], 5, 4, 6, 0.0, None) == EINVAL
+    assert lib.birkhoff_eot_bwd(Q[0], Q[1], Q[2], 0, Q[3], 5, 4, 6, math.nan, None) == EINVAL
+    assert lib.birkhoff_eot_bwd(None, None, None, 0, None, 0, 4, 6, 0.5, None) == 0
+    for k in range(4):
+        ptrs = list(Q)
+        ptrs[k] = None
+        assert lib.birkhoff_eot_bwd(ptrs[0], ptrs[1], ptrs[2], 0, ptrs[3], 5, 4, 6, 0.5, None) == EINVAL
+        ptrs[k] = Q[k] + 8
+        assert lib.birkhoff_eot_bwd(ptrs[0], ptrs[1], ptrs[2], 0, ptrs[3], 5, 4, 6, 0.5, None) == EALIGN
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
