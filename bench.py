@@ -83,6 +83,115 @@ def cpu_baseline(w, target_s: float = 10.0):
                       % (Bs, "all of it" if Bs == w.B else "a prefix", dt)}
 
 
+def eot_cpu_baseline(w, target_s: float = 10.0):
+    """The float64 oracle for the general problem (certified plan + eq (13)
+    backward) on a bounded sample of the workload, on this host's cores."""
+    import oracle
+    from birkhoff_projection_amd import workloads as W
+
+    def run(Bs):
+        M, a, b = W.make_eot(w, B=Bs)
+        G = W.make_eot_upstream(w, B=Bs)
+        M, a, b, G = (x.astype("float64") for x in (M, a, b, G))
+        t0 = time.perf_counter()
+        T, _, _ = oracle.eot_project(M, a, b, w.eta, sk_cap=w.sk_cap)
+        oracle.eot_bwd(T, G, a, b, w.eta)
+        return time.perf_counter() - t0
+
+    probe = 8192
+    dt = run(probe)
+    Bs = int(min(w.B, max(probe, probe * target_s / max(dt, 1e-6))))
+    dt = run(Bs)
+    return {"value": Bs / dt, "unit": "problems/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": "the first %d problems of the same seeded workload (%s), float64: Sinkhorn to 1e-13 "
+                      "with a Newton cross-check, then the eq (13) backward; %.1f s wall"
+                      % (Bs, "all of it" if Bs == w.B else "a prefix", dt)}
+
+
+def eot_report(w, args, dev):
+    """A general entropic-OT workload: the step is birkhoff_eot_fwd then
+    birkhoff_eot_bwd (the backward at the forward's plan)."""
+    import torch
+
+    import birkhoff_projection_amd as bp
+    from birkhoff_projection_amd import build as hipbuild
+    from birkhoff_projection_amd import workloads as W
+
+    B, n, m = w.B, w.n, w.m
+    M, a, b = W.make_eot(w)
+    G = W.make_eot_upstream(w)
+    sets = []
+    for _ in range(2):
+        st = {k: torch.from_numpy(v).to(dev) for k, v in (("M", M), ("a", a), ("b", b), ("G", G))}
+        st["T"] = torch.empty((B, n, m), dtype=torch.float32, device=dev)
+        st["D"] = torch.empty((B, n, m), dtype=torch.float32, device=dev)
+        st["dual"] = torch.empty((B, m), dtype=torch.float32, device=dev)
+        sets.append(st)
+    del M, a, b, G
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+
+    def run_fwd(s):
+        bp.birkhoff_eot_fwd(s["M"], s["a"], s["b"], s["T"], s["dual"], None, w.eta, w.tol, w.max_iter, stream)
+
+    def run_bwd(s):
+        bp.birkhoff_eot_bwd(s["T"], s["G"], s["a"], s["D"], w.eta, stream)
+
+    def step(s):
+        run_fwd(s)
+        run_bwd(s)
+
+    def timed(fn, K):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(K):
+            fn(sets[i % 2])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+
+    for i in range(args.warmup):
+        step(sets[i % 2])
+    torch.cuda.synchronize()
+    K = args.steps
+    ms_step = timed(step, K)
+    fwd_ms = timed(run_fwd, K)
+    bwd_ms = timed(run_bwd, K)
+    iters = torch.empty(B, dtype=torch.int32, device=dev)
+    st = sets[0]
+    bp.birkhoff_eot_fwd(st["M"], st["a"], st["b"], st["T"], st["dual"], iters, w.eta, w.tol, w.max_iter, stream)
+    torch.cuda.synchronize()
+    it = iters.cpu().numpy()
+    waves = it[: (B // 64) * 64].reshape(-1, 64)
+
+    b_fwd = W.eot_bytes_per_problem(n, m, "fwd", w.shared) * B
+    b_bwd = W.eot_bytes_per_problem(n, m, "bwd", w.shared) * B
+    kern = {"birkhoff_eot_fwd": (fwd_ms, b_fwd), "birkhoff_eot_bwd": (bwd_ms, b_bwd)}
+    dom = max(kern, key=lambda k: kern[k][0])
+    d_ms, d_bytes = kern[dom]
+    achieved = d_bytes / (d_ms * 1e-3) / 1e9
+    digest = hipbuild.kernel_source_digest()
+    return {
+        "metric": "%dx%d entropic OT plans/sec (fwd+bwd, fp32, general cost / marginals / eta) on 1 MI355X; "
+                  "%% HBM roofline" % (n, m),
+        "value": B / (ms_step * 1e-3), "unit": "problems/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "%s: %s" % (w.key, w.title), "B": B, "n": n, "m": m, "eta": w.eta,
+                   "shared_marginals": w.shared, "passes": "fwd+bwd", "tol": w.tol, "max_iter": w.max_iter},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.key, dom, digest),
+                     "algorithmic_bytes_per_launch": d_bytes, "avg_launch_ms": d_ms},
+        "kernels_ms": {"birkhoff_eot_fwd": fwd_ms, "birkhoff_eot_bwd": bwd_ms},
+        "kernels_hbm_frac": {k: v[1] / (v[0] * 1e-3) / 1e9 / HBM_PEAK_GBS for k, v in kern.items()},
+        "newton": {"iterations_mean": float(it[it >= 0].mean()), "wave_max_mean": float(waves.max(1).mean()),
+                   "unconverged": int((it < 0).sum())},
+        "kernel_digest": digest,
+    }
+
+
 def forward_only_report(w, args, dev):
     """A forward-only workload (the hard-conditioning one): the timed step is one
     birkhoff_fwd launch; the fixed 20-sweep Sinkhorn-Knopp kernel is timed on the
@@ -191,14 +300,19 @@ def main() -> int:
     import birkhoff_projection_amd as bp
     from birkhoff_projection_amd import workloads as W
 
-    w = W.WORKLOADS[args.workload]
+    if args.workload not in W.WORKLOADS and args.workload not in W.EOT_WORKLOADS:
+        print("unknown workload %r (have %s)" % (args.workload, sorted(W.WORKLOADS) + sorted(W.EOT_WORKLOADS)),
+              file=sys.stderr)
+        return 2
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     bp.load_library()
-    if w.passes == "fwd":
-        out = forward_only_report(w, args, dev)
+    if args.workload in W.EOT_WORKLOADS:
+        w = W.EOT_WORKLOADS[args.workload]
+        out = eot_report(w, args, dev)
     else:
-        out = forward_backward_report(w, args, dev)
+        w = W.WORKLOADS[args.workload]
+        out = forward_only_report(w, args, dev) if w.passes == "fwd" else forward_backward_report(w, args, dev)
     if args.calibrate_copy > 0:
         src = torch.ones(args.calibrate_copy << 18, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -208,7 +322,8 @@ def main() -> int:
         out["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": src.numel() * 4}
         del src, dst
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        out["cpu_baseline"] = (eot_cpu_baseline(w, args.cpu_seconds) if args.workload in W.EOT_WORKLOADS
+                               else cpu_baseline(w, args.cpu_seconds))
     print(json.dumps(out), flush=True)
     return 0
 

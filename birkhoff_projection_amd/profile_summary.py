@@ -32,7 +32,8 @@ ROOT = pathlib.Path(__file__).resolve().parent.parent
 # device kernel -> the C-ABI entry point that launches it
 ENTRY = (("newton_fwd_kernel", "birkhoff_fwd"), ("implicit_bwd_from_T_kernel", "birkhoff_bwd_from_T"),
          ("implicit_bwd_kernel", "birkhoff_bwd"),
-         ("sinkhorn_kernel", "sinkhorn_fwd"), ("fused_fwd_bwd_kernel", "birkhoff_fwd_bwd"))
+         ("sinkhorn_kernel", "sinkhorn_fwd"), ("fused_fwd_bwd_kernel", "birkhoff_fwd_bwd"),
+         ("eot_fwd_kernel", "birkhoff_eot_fwd"), ("eot_bwd_kernel", "birkhoff_eot_bwd"))
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
