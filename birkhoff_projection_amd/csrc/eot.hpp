@@ -206,17 +206,23 @@ __device__ __forceinline__ void hessian(const float (&S)[N * M], const float (&a
     for (int j = 0; j < K1; ++j) h[Tri<M>::at(j, j)] = dg[j];
 }
 
-// e^x - 1 - x and log(1 + q) - q, both of second order in the argument,
-// with their Taylor series below 1/16 (truncation below 1e-9 relative).
-// `ex` must be e^x; `l1p` must be log(1 + q) (used at and above 1/16).
-__device__ __forceinline__ float expm1_minus_x(float x, float ex) {
+// e^x - 1 and e^x - 1 - x (the latter of second order in x) from one Taylor
+// polynomial below |x| = 1/16 (e^x - 1 - x = x^2 p(x), truncation below 1e-9
+// relative), from `ex` = e^x elsewhere.
+__device__ __forceinline__ void expm1_pair(float x, float ex, float& em, float& xm) {
     float p = fmaf(x, 1.0f / 5040.0f, 1.0f / 720.0f);
     p = fmaf(x, p, 1.0f / 120.0f);
     p = fmaf(x, p, 1.0f / 24.0f);
     p = fmaf(x, p, 1.0f / 6.0f);
     p = fmaf(x, p, 0.5f);
-    return fabsf(x) < 0.0625f ? x * x * p : (ex - 1.0f) - x;
+    const float x2p = x * x * p;
+    const bool small = fabsf(x) < 0.0625f;
+    em = small ? x + x2p : ex - 1.0f;
+    xm = small ? x2p : (ex - 1.0f) - x;
 }
+
+// log(1 + q) - q, of second order in q: Taylor series below |q| = 1/16
+// (truncation below 1e-9 relative), `l1p` = log(1 + q) elsewhere.
 
 __device__ __forceinline__ float log1p_minus_x(float q, float l1p) {
     float p = fmaf(q, 1.0f / 9.0f, -1.0f / 8.0f);
@@ -251,8 +257,9 @@ __device__ __forceinline__ float trial_point(const float (&S)[N * M], const floa
 #pragma unroll
     for (int j = 0; j < K1; ++j) {
         e[j] = ex2(s[j] * kLog2e);
-        em[j] = expm1_from(s[j], e[j]);
-        df = fmaf(c[j], expm1_minus_x(s[j], e[j]), fmaf(g[j], s[j], df));
+        float xm;
+        expm1_pair(s[j], e[j], em[j], xm);
+        df = fmaf(c[j], xm, fmaf(g[j], s[j], df));
     }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
@@ -353,7 +360,7 @@ struct Lanes {
     __device__ __forceinline__ int64_t problem() const { return base + lane; }
 };
 
-// Forward: Newton on the reduced dual (eq 8) from z = 0 until the column
+// Forward: Newton on the reduced dual (eq 8) from z = log(b / b_{m-1}) until the column
 // marginals are met to `tol` (absolute) or `max_iter` updates; rows are met by
 // construction.  Step sizes 1, 1/2, 1/10, 1/20, 1/100, the first that lowers
 // both the objective and the gradient norm is taken; otherwise one Sinkhorn
@@ -377,15 +384,19 @@ eot_fwd_kernel(const float* __restrict__ cost, const float* __restrict__ a_in, c
     float a[N], b[M];
     load_marginal<N>(a_in, shared, ln.base, ln.nvalid, lds, ln.lane, a);
     load_marginal<M>(b_in, shared, ln.base, ln.nvalid, lds, ln.lane, b);
+    // start at z = log(b / b_{m-1}) (base 2 here): the optimum when the cost is
+    // constant (plan a b^T / sum(b)), and z = 0 when b = 1 as for the Birkhoff
+    // projection; lanes past the end (b = 0) start at 0
     float S[N * M], y[K1], c[M];
-#pragma unroll
-    for (int j = 0; j < K1; ++j) y[j] = 0.0f;
     {
+        const float lbm = ln.valid() ? lg2(b[K1]) : 0.0f;
+#pragma unroll
+        for (int j = 0; j < K1; ++j) y[j] = ln.valid() ? lg2(b[j]) - lbm : 0.0f;
         float L[N * M];
         Items<N * M>::load(cost + ln.base * (N * M), ln.nvalid * (N * M), lds, ln.lane, L);
 #pragma unroll
         for (int k = 0; k < N * M; ++k) L[k] *= lscale;
-        softmax_rows0<M, N>(L, S);
+        softmax_rows<M, N>(L, y, S);
     }
     col_sums<N, M>(S, a, c);
     float res = ln.valid() ? col_residual<M>(c, b) : 0.0f;

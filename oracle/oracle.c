@@ -481,7 +481,10 @@ static void eot_eval_T(const double *M, const double *a, int n, int m, double et
     }
 }
 
-/* Newton's method on the reduced dual (eq 8), from x = 0:
+/* Newton's method on the reduced dual (eq 8), from x^(0) = eta (log b_{-m} - log b_m)
+ * (the pages leave x^(0) open; this start is x = 0 when b = 1, as in the
+ * Birkhoff case, and is already the optimum when the cost is constant, whose
+ * plan is a b^T / sum(b)):
  *   gradient  g = c_{-m} - b_{-m}                                   (eq 9)
  *   Hessian   eta^-1 [diag(c_{-m}) - T_{-m}^T diag(a)^-1 T_{-m}]    (eq 9)
  * with the step-size rule and Sinkhorn fallback of [B] section 2.2, as in
@@ -499,7 +502,7 @@ static int eot_newton_one(const double *M, const double *a, const double *b, int
     double hess[ORACLE_NMAX * ORACLE_NMAX];
     double bt[ORACLE_NMAX], Tt[ORACLE_NMAX * ORACLE_NMAX], ct[ORACLE_NMAX];
     double alpha[ORACLE_NMAX];
-    for (int j = 0; j < m; ++j) beta[j] = 0.0;
+    for (int j = 0; j < m; ++j) beta[j] = eta * (log(b[j]) - log(b[m - 1]));
     eot_eval_T(M, a, n, m, eta, beta, T, c);
     int it = 0, conv = 0;
     for (;;) {

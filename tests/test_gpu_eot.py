@@ -113,11 +113,13 @@ def test_forward_ragged_batches(n, m, B):
 @pytest.mark.parametrize("eta", [0.125, 0.25, 2.0, 8.0])
 def test_forward_eta_range(eta):
     """Small eta sharpens the plans (cost / eta up to ~30): more Newton updates,
-    same gates."""
+    same gates.  At eta = 1/8 the step rule crawls on a few problems (the
+    float64 oracle's Newton, run with the same rule, needs up to ~150 updates
+    on 20,000 such problems), so the cap is raised to 200."""
     w = workload(4, 6, eta=eta, seed=62)
     M, a, b = W.make_eot(w, B=2048)
     print("eot eta=%g" % eta, flush=True)
-    T, dual, iters = bp.eot_plan(dev(M), dev(a), dev(b), eta, max_iter=100, with_iters=True)
+    T, dual, iters = bp.eot_plan(dev(M), dev(a), dev(b), eta, max_iter=200, with_iters=True)
     torch.cuda.synchronize()
     check_forward(M, a, b, eta, T, dual, iters)
 

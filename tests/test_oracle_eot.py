@@ -206,8 +206,9 @@ def test_reduced_dual_with_library_minimiser(n, m):
 
 @pytest.mark.parametrize("eta", [0.3, 3.0])
 def test_first_newton_step_matches_finite_difference_newton(eta):
-    """One Newton update from x = 0 on a mild problem (the full step is taken):
-    x1 = -H^{-1} g, with g and H the finite-difference gradient and Hessian of eq (8)."""
+    """One Newton update from x0 = eta (log b_{-m} - log b_m) on a mild problem (the full
+    step is taken): x1 = x0 - H^{-1} g, with g and H the finite-difference gradient and
+    Hessian of eq (8) at x0."""
     rng = np.random.default_rng(108)
     n, m = 4, 5
     M, a, b = problem(rng, 6, n, m, sigma=0.3 * eta)
@@ -221,12 +222,24 @@ def test_first_newton_step_matches_finite_difference_newton(eta):
             return eta * aq.sum() - alpha @ aq - beta @ bq
 
         k, h = m - 1, 1e-4 * eta
+        x0 = eta * (np.log(bq[:-1]) - np.log(bq[-1]))
         E = np.eye(k) * h
-        g = np.array([(f(E[i]) - f(-E[i])) / (2 * h) for i in range(k)])
-        Hs = np.array([[(f(E[i] + E[j]) - f(E[i] - E[j]) - f(-E[i] + E[j]) + f(-E[i] - E[j])) / (4 * h * h)
-                        for j in range(k)] for i in range(k)])
-        x1 = -np.linalg.solve(Hs, g)
+        g = np.array([(f(x0 + E[i]) - f(x0 - E[i])) / (2 * h) for i in range(k)])
+        Hs = np.array([[(f(x0 + E[i] + E[j]) - f(x0 + E[i] - E[j]) - f(x0 - E[i] + E[j]) + f(x0 - E[i] - E[j]))
+                        / (4 * h * h) for j in range(k)] for i in range(k)])
+        x1 = x0 - np.linalg.solve(Hs, g)
         np.testing.assert_allclose(beta1[q, :-1], x1, rtol=1e-5, atol=1e-7 * eta)
+
+
+def test_constant_cost_needs_no_update():
+    """A constant cost has the plan a b^T / sum(b); the start x0 = eta log(b_{-m} / b_m)
+    is already optimal, so Newton stops before its first update."""
+    rng = np.random.default_rng(115)
+    M, a, b = problem(rng, 8, 3, 6)
+    M[:] = 0.7
+    T, beta, it = oracle.eot_newton(M, a, b, 0.4, tol=1e-12)
+    assert (it == 0).all()
+    np.testing.assert_allclose(T, a[:, :, None] * b[:, None, :], rtol=0, atol=1e-14)
 
 
 @pytest.mark.parametrize("n,m", [(3, 5), (5, 3), (4, 4), (8, 8), (1, 4)])
