@@ -469,7 +469,7 @@ eot_fwd_kernel(const float* __restrict__ cost, const float* __restrict__ a_in, c
         beta[K1] = 0.0f;
         Items<M>::store(beta, lds, ln.lane, dual + ln.base * M, ln.nvalid * M);
     }
-    if (kStats && ln.valid()) iters[ln.problem()] = (res <= tol) ? it : -1;
+    if (kStats && ln.valid()) __builtin_nontemporal_store((res <= tol) ? it : -1, iters + ln.problem());
 }
 
 // Backward, eq (13): D = dl/dM from the plan T* and upstream G = dl/dT,

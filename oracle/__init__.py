@@ -84,6 +84,10 @@ def _load():
     lib.oracle_eot_bwd.argtypes = [dp, dp, dp, dp, i64, ci, ci, cd, dp]
     lib.oracle_eot_residuals.restype = ci
     lib.oracle_eot_residuals.argtypes = [dp, dp, dp, i64, ci, ci, dp]
+    lib.oracle_mix.restype = ci
+    lib.oracle_mix.argtypes = [dp, dp, i64, ci, i64, dp]
+    lib.oracle_mix_bwd.restype = ci
+    lib.oracle_mix_bwd.argtypes = [dp, dp, dp, i64, ci, i64, dp, dp]
     _lib = lib
     return lib
 
@@ -258,3 +262,38 @@ def eot_residuals(T, a, b):
     r = np.empty(B)
     _check(_load().oracle_eot_residuals(_p(T), _p(a), _p(b), B, n, m, _p(r)), "eot_residuals")
     return r
+
+
+# ---------------------------------------------------------------------------
+# mHC consumer: y = T x for the n x C hidden matrix x of each token.
+# ---------------------------------------------------------------------------
+
+def _streams(x, B, n):
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    if x.ndim != 3 or x.shape[0] != B or x.shape[1] != n:
+        raise ValueError("expected [%d, %d, C], got %r" % (B, n, x.shape))
+    return x
+
+
+def mix(T, x):
+    """y = T x per token: T [B, n, n], x [B, n, C] -> y [B, n, C]."""
+    T = _mat(T)
+    B, n, _ = T.shape
+    x = _streams(x, B, n)
+    y = np.empty_like(x)
+    _check(_load().oracle_mix(_p(T), _p(x), B, n, x.shape[2], _p(y)), "mix")
+    return y
+
+
+def mix_bwd(T, x, dy):
+    """Backward of y = T x: returns (dx = T^T dy, dT = dy x^T)."""
+    T = _mat(T)
+    B, n, _ = T.shape
+    x = _streams(x, B, n)
+    dy = _streams(dy, B, n)
+    if dy.shape != x.shape:
+        raise ValueError("x and dy shapes differ")
+    dx = np.empty_like(x)
+    dT = np.empty_like(T)
+    _check(_load().oracle_mix_bwd(_p(T), _p(x), _p(dy), B, n, x.shape[2], _p(dx), _p(dT)), "mix_bwd")
+    return dx, dT

@@ -36,6 +36,12 @@
  * symmetries, the Birkhoff special case, finite differences, shift invariants
  * and unrolled autograd for eq (13).
  *
+ * oracle_mix / oracle_mix_bwd are the consumer of the projection: the
+ * residual-stream mixing y = H_res x of the mHC layer update ([P] section 2.1)
+ * and its backward, pinned against library matmuls, exact properties of
+ * doubly stochastic and permutation matrices, autograd, and finite differences
+ * through the projection.
+ *
  * Parity pins.  Every exported function is pinned by tests that do not call
  * this code for the expected value: the n = 2 closed form, exactly known
  * fixed points (doubly stochastic inputs with row/column shifts), rank-one
@@ -813,5 +819,56 @@ int oracle_eot_residuals(const double *T, const double *a, const double *b, int6
     if (eot_bad_args(B, n, m, 1.0, T) || (B > 0 && (!a || !b || !res))) return -1;
 #pragma omp parallel for schedule(static)
     for (int64_t q = 0; q < B; ++q) res[q] = eot_marginal_residual(T + q * n * m, a + q * n, b + q * m, n, m);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* mHC consumer: the residual-stream mixing H_res x ([P] section 2.1)   */
+/* ------------------------------------------------------------------ */
+/* The projected matrix is the residual mapping H_res of the layer update
+ * x_{l+1} = H_res x_l + H_post^T F(H_pre x_l) ([P] section 2.1), applied to the
+ * n x C hidden matrix x of each token:  y = T x  (y_ic = sum_j T_ij x_jc).
+ * Its backward, for upstream dy = dL/dy:  dx = T^T dy  and  dT = dy x^T
+ * (dT_ij = sum_c dy_ic x_jc), which the eq (13) backward (oracle_bwd) turns into
+ * dL/dH.  Arrays: T [B, n, n], x, y, dy, dx [B, n, C], dT [B, n, n]. */
+
+int oracle_mix(const double *T, const double *x, int64_t B, int n, int64_t C, double *y)
+{
+    if (B < 0 || n < 1 || n > ORACLE_NMAX || C < 0 || (B > 0 && C > 0 && (!T || !x || !y))) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t q = 0; q < B; ++q) {
+        const double *Tq = T + q * n * n, *xq = x + q * n * C;
+        double *yq = y + q * n * C;
+        for (int i = 0; i < n; ++i)
+            for (int64_t c = 0; c < C; ++c) {
+                double s = 0.0;
+                for (int j = 0; j < n; ++j) s += Tq[i * n + j] * xq[j * C + c];
+                yq[i * C + c] = s;
+            }
+    }
+    return 0;
+}
+
+int oracle_mix_bwd(const double *T, const double *x, const double *dy, int64_t B, int n, int64_t C, double *dx,
+                   double *dT)
+{
+    if (B < 0 || n < 1 || n > ORACLE_NMAX || C < 0 || (B > 0 && (!T || !x || !dy || !dx || !dT))) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t q = 0; q < B; ++q) {
+        const double *Tq = T + q * n * n, *xq = x + q * n * C, *dyq = dy + q * n * C;
+        double *dxq = dx + q * n * C, *dTq = dT + q * n * n;
+        for (int j = 0; j < n; ++j)
+            for (int64_t c = 0; c < C; ++c) {
+                double s = 0.0;
+                for (int i = 0; i < n; ++i) s += Tq[i * n + j] * dyq[i * C + c];
+                dxq[j * C + c] = s;
+            }
+        for (int i = 0; i < n; ++i)
+            for (int j = 0; j < n; ++j) {
+                double s = 0.0;
+                for (int64_t c = 0; c < C; ++c) s += dyq[i * C + c] * xq[j * C + c];
+                dTq[i * n + j] = s;
+            }
+    }
     return 0;
 }

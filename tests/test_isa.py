@@ -1,7 +1,8 @@
 """Code-generation checks on the gfx950 assembly of the kernels (CPU only: hipcc
 cross-compiles).  They pin properties the measured performance depends on:
 every matrix / dual store is non-temporal, the n = 4 kernels keep their
-occupancy and spill nothing, and the n = 8 loops keep four waves per SIMD."""
+occupancy and spill nothing, the n = 8 loops keep four waves per SIMD, and the
+general-OT kernels spill nothing and stream their stores too."""
 import re
 import shutil
 import subprocess
@@ -14,15 +15,25 @@ pytestmark = pytest.mark.skipif(shutil.which("hipcc") is None and not hipbuild.o
                                 reason="hipcc not available")
 
 
-@pytest.fixture(scope="module")
-def asm(tmp_path_factory):
-    out = tmp_path_factory.mktemp("isa") / "birkhoff.s"
+def compile_asm(tmp_path_factory, source):
+    out = tmp_path_factory.mktemp("isa") / (source + ".s")
     cmd = [hipbuild.hipcc(), "--offload-arch=%s" % hipbuild.ARCH, "-O3", "-std=c++17",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-I", str(hipbuild.ROOT / "include"), "-I", str(hipbuild.CSRC),
-           "--cuda-device-only", "-S", str(hipbuild.SOURCES[0]), "-o", str(out)]
+           "--cuda-device-only", "-S", str(hipbuild.CSRC / source), "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True)
     return out.read_text()
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    return compile_asm(tmp_path_factory, "birkhoff.hip")
+
+
+@pytest.fixture(scope="module")
+def asm_eot(tmp_path_factory):
+    """The general-OT kernels for n = 4 and 5 rows (every column count)."""
+    return compile_asm(tmp_path_factory, "eot_rows_45.hip")
 
 
 def kernels(asm):
@@ -60,3 +71,14 @@ def test_n8_forward_keeps_four_waves(asm):
     assert hits
     for _, vgpr, scratch, o in hits:
         assert o >= 4, (vgpr, scratch, o)
+
+
+def test_eot_kernels_stream_and_do_not_spill(asm_eot):
+    ks = kernels(asm_eot)
+    assert len(ks) == 2 * 7 * 3   # n = 4, 5; m = 2..8; forward with and without counts, backward
+    for name, (body, vgpr, scratch, occ) in ks.items():
+        assert scratch == 0, (name, vgpr)
+        for line in re.findall(r"^\s+global_store_dword(?:x4)?\s.*$", body, flags=re.M):
+            assert line.rstrip().endswith(" nt"), (name, line)
+    small = [v for k, v in ks.items() if "eot_fwd_kernelILi4ELi4E" in k]
+    assert small and all(o >= 4 for _, _, _, o in small)

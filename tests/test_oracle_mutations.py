@@ -1,8 +1,9 @@
 """Plant plausible slips in a copy of the oracle (on the CPU) and check that the
 pins in test_oracle.py catch every one of them.
 
-Both pin files (test_oracle.py for the Birkhoff functions, test_oracle_eot.py
-for the general entropic OT) run against every mutant.  Each mutant is oracle.c
+The pin files (test_oracle.py for the Birkhoff functions, test_oracle_eot.py
+for the general entropic OT, test_oracle_mix.py for the stream mixing) run
+against every mutant.  Each mutant is oracle.c
 with one textual edit (a flipped sign, a dropped term,
 a transposed index, a lost gauge), compiled to a temporary library and loaded
 by the oracle's Python wrapper through ORACLE_LIB in a child pytest run.
@@ -60,6 +61,13 @@ MUTANTS = {
     "eot_bwd_rhs_drop_inv_a": ("tm += T[i * m + j] * mur[i] / a[i];", "tm += T[i * m + j] * mur[i];"),
     "eot_bwd_delta_drop_inv_a": ("for (int i = 0; i < n; ++i) p += T[i * m + j] / a[i] * T[i * m + k];",
                                  "for (int i = 0; i < n; ++i) p += T[i * m + j] * T[i * m + k];"),
+    # mHC consumer mixing y = T x and its backward
+    "mix_transposed": ("for (int j = 0; j < n; ++j) s += Tq[i * n + j] * xq[j * C + c];",
+                       "for (int j = 0; j < n; ++j) s += Tq[j * n + i] * xq[j * C + c];"),
+    "mix_bwd_dx_untransposed": ("for (int i = 0; i < n; ++i) s += Tq[i * n + j] * dyq[i * C + c];",
+                                "for (int i = 0; i < n; ++i) s += Tq[j * n + i] * dyq[i * C + c];"),
+    "mix_bwd_dT_transposed": ("for (int64_t c = 0; c < C; ++c) s += dyq[i * C + c] * xq[j * C + c];",
+                              "for (int64_t c = 0; c < C; ++c) s += dyq[j * C + c] * xq[i * C + c];"),
 }
 
 
@@ -73,7 +81,8 @@ def _run_mutant(name, tmp):
                    check=True)
     env = dict(os.environ, ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        str(ROOT / "tests" / "test_oracle.py"), str(ROOT / "tests" / "test_oracle_eot.py")],
+                        str(ROOT / "tests" / "test_oracle.py"), str(ROOT / "tests" / "test_oracle_eot.py"),
+                        str(ROOT / "tests" / "test_oracle_mix.py")],
                        cwd=str(ROOT), env=env, capture_output=True, text=True, timeout=600)
     return name, r.returncode, r.stdout[-400:]
 
