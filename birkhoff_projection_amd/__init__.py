@@ -23,9 +23,11 @@ __all__ = [
     "birkhoff_fwd", "birkhoff_fwd_ex", "birkhoff_bwd", "birkhoff_bwd_from_T", "sinkhorn_fwd",
     "birkhoff_fwd_bf16", "birkhoff_bwd_bf16", "birkhoff_fwd_bwd", "birkhoff_fwd_bwd_bf16",
     "birkhoff_eot_fwd", "birkhoff_eot_bwd",
+    "birkhoff_fwd_mix", "birkhoff_fwd_mix_bf16", "birkhoff_mix_bwd", "birkhoff_mix_bwd_bf16",
     "birkhoff_strerror", "birkhoff_abi_version",
     "project", "project_bwd", "project_fwd_bwd", "sinkhorn", "BirkhoffProjection",
     "eot_plan", "eot_plan_bwd", "EntropicOT",
+    "project_mix", "project_mix_bwd", "ProjectMix",
 ]
 
 _PKG = pathlib.Path(__file__).resolve().parent
@@ -67,6 +69,10 @@ def load_library():
         "birkhoff_fwd_bwd_bf16": [vp, vp, vp, vp, vp, i64, ci, cf, ci, vp],
         "birkhoff_eot_fwd": [vp, vp, vp, ci, vp, vp, vp, i64, ci, ci, cf, cf, ci, vp],
         "birkhoff_eot_bwd": [vp, vp, vp, ci, vp, i64, ci, ci, cf, vp],
+        "birkhoff_fwd_mix": [vp, vp, vp, vp, vp, i64, ci, i64, cf, ci, vp],
+        "birkhoff_fwd_mix_bf16": [vp, vp, vp, vp, vp, i64, ci, i64, cf, ci, vp],
+        "birkhoff_mix_bwd": [vp, vp, vp, vp, vp, i64, ci, i64, vp],
+        "birkhoff_mix_bwd_bf16": [vp, vp, vp, vp, vp, i64, ci, i64, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -327,6 +333,71 @@ def birkhoff_eot_bwd(T, dT, a, dcost, eta: float = 1.0, stream=None) -> None:
           _stream_handle(stream, dev))
 
 
+def _streams(x, name, B=None, C=None, bf16=False):
+    """Hidden states [B, 4, C]: float32, or bfloat16 / 16-bit bf16 patterns for the _bf16 entries."""
+    torch = _torch()
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    ok = (x.dtype in (torch.bfloat16, torch.int16, getattr(torch, "uint16", torch.int16))) if bf16 \
+        else x.dtype == torch.float32
+    if not ok:
+        raise TypeError("%s has dtype %s" % (name, x.dtype))
+    if not x.is_cuda or not x.is_contiguous() or x.dim() != 3 or x.shape[1] != 4:
+        raise ValueError("%s must be a contiguous GPU tensor of shape [B, 4, C], got %s" % (name, tuple(x.shape)))
+    if B is not None and (x.shape[0] != B or x.shape[2] != C):
+        raise ValueError("%s must have shape [%d, 4, %d], got %s" % (name, B, C, tuple(x.shape)))
+    return x
+
+
+def _fwd_mix(name, bf16, logits, x, T, dual, y, tol, max_iter, stream):
+    torch = _torch()
+    _mats(logits, "logits", torch.float32)
+    B, n = logits.shape[0], logits.shape[1]
+    _streams(x, "x", bf16=bf16)
+    C = x.shape[2]
+    _streams(x, "x", B, C, bf16)
+    _streams(y, "y", B, C, bf16)
+    _mats(T, "T", torch.float32, B, n)
+    _vec(dual, "dual", B, n, torch.float32)
+    dev = _same_device(logits, x, T, dual, y)
+    _call(name, dev, _p(logits), _p(x), _p(T), _p(dual), _p(y), B, n, C, float(tol), int(max_iter),
+          _stream_handle(stream, dev))
+
+
+def birkhoff_fwd_mix(logits, x, T, dual, y, tol: float = 1e-6, max_iter: int = 50, stream=None) -> None:
+    """Projection of logits [B,4,4] fused with y = T x for hidden states x [B,4,C] (fp32)."""
+    _fwd_mix("birkhoff_fwd_mix", False, logits, x, T, dual, y, tol, max_iter, stream)
+
+
+def birkhoff_fwd_mix_bf16(logits, x, T, dual, y, tol: float = 1e-6, max_iter: int = 50, stream=None) -> None:
+    """As birkhoff_fwd_mix with bf16 hidden states x and y (fp32 logits, T, dual)."""
+    _fwd_mix("birkhoff_fwd_mix_bf16", True, logits, x, T, dual, y, tol, max_iter, stream)
+
+
+def _mix_bwd(name, bf16, T, x, dy, dx, dH, stream):
+    torch = _torch()
+    _mats(T, "T", torch.float32)
+    B, n = T.shape[0], T.shape[1]
+    _streams(x, "x", bf16=bf16)
+    C = x.shape[2]
+    _streams(x, "x", B, C, bf16)
+    _streams(dy, "dy", B, C, bf16)
+    _streams(dx, "dx", B, C, bf16)
+    _mats(dH, "dH", torch.float32, B, n)
+    dev = _same_device(T, x, dy, dx, dH)
+    _call(name, dev, _p(T), _p(x), _p(dy), _p(dx), _p(dH), B, n, C, _stream_handle(stream, dev))
+
+
+def birkhoff_mix_bwd(T, x, dy, dx, dH, stream=None) -> None:
+    """Backward of y = T x and of the projection: dx = T^T dy, dH by eq (13) from dT = dy x^T (fp32)."""
+    _mix_bwd("birkhoff_mix_bwd", False, T, x, dy, dx, dH, stream)
+
+
+def birkhoff_mix_bwd_bf16(T, x, dy, dx, dH, stream=None) -> None:
+    """As birkhoff_mix_bwd with bf16 hidden states x, dy and dx."""
+    _mix_bwd("birkhoff_mix_bwd_bf16", True, T, x, dy, dx, dH, stream)
+
+
 # ------------------------------------------------------- allocating helpers
 
 def project(logits, tol: float = 1e-6, max_iter: int = 50, stream=None):
@@ -392,6 +463,32 @@ def eot_plan_bwd(T, dT, a, eta: float = 1.0, stream=None):
     return dcost
 
 
+def project_mix(logits, x, tol: float = 1e-6, max_iter: int = 50, stream=None):
+    """Project logits [B,4,4] and mix hidden states x [B,4,C]: returns (T, dual, y)."""
+    torch = _torch()
+    B, n = logits.shape[0], logits.shape[1]
+    T = torch.empty((B, n, n), dtype=torch.float32, device=logits.device)
+    dual = torch.empty((B, n), dtype=torch.float32, device=logits.device)
+    y = torch.empty_like(x)
+    if x.dtype == torch.float32:
+        birkhoff_fwd_mix(logits, x, T, dual, y, tol, max_iter, stream)
+    else:
+        birkhoff_fwd_mix_bf16(logits, x, T, dual, y, tol, max_iter, stream)
+    return T, dual, y
+
+
+def project_mix_bwd(T, x, dy, stream=None):
+    """Backward of project_mix: returns (dH, dx)."""
+    torch = _torch()
+    dH = torch.empty_like(T)
+    dx = torch.empty_like(x)
+    if x.dtype == torch.float32:
+        birkhoff_mix_bwd(T, x, dy, dx, dH, stream)
+    else:
+        birkhoff_mix_bwd_bf16(T, x, dy, dx, dH, stream)
+    return dH, dx
+
+
 def _autograd_function():
     torch = _torch()
 
@@ -429,7 +526,23 @@ def _autograd_function():
             T, a = ctx.saved_tensors
             return eot_plan_bwd(T, dT.contiguous(), a, ctx.eta), None, None, None, None, None
 
-    return {"BirkhoffProjection": BirkhoffProjection, "EntropicOT": EntropicOT}
+    class ProjectMix(torch.autograd.Function):
+        """y = proj_KL(exp(logits)) x per token (the mHC residual mixing H_res x),
+        differentiable in both the logits (eq 13) and x.  Saves (T, x)."""
+
+        @staticmethod
+        def forward(ctx, logits, x, tol: float = 1e-6, max_iter: int = 50):
+            T, _, y = project_mix(logits.contiguous(), x.contiguous(), tol, max_iter)
+            ctx.save_for_backward(T, x)
+            return y
+
+        @staticmethod
+        def backward(ctx, dy):
+            T, x = ctx.saved_tensors
+            dH, dx = project_mix_bwd(T, x.contiguous(), dy.contiguous())
+            return dH, dx, None, None
+
+    return {"BirkhoffProjection": BirkhoffProjection, "EntropicOT": EntropicOT, "ProjectMix": ProjectMix}
 
 
 class _LazyFunction:
@@ -446,3 +559,4 @@ class _LazyFunction:
 
 BirkhoffProjection = _LazyFunction("BirkhoffProjection")
 EntropicOT = _LazyFunction("EntropicOT")
+ProjectMix = _LazyFunction("ProjectMix")

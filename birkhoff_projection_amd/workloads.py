@@ -237,3 +237,76 @@ def eot_bytes_per_problem(n: int, m: int, passes: str, shared: bool) -> int:
     if passes == "fwd+bwd":
         return fwd + bwd
     raise ValueError("unknown passes %r" % (passes,))
+
+
+# ---------------------------------------------------------------------------
+# The projection's consumer: y = H_res x for per-token hidden states x [B, 4, C]
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class MixWorkload:
+    key: str
+    title: str
+    B: int                       # tokens (one 4 x 4 logit matrix each)
+    C: int                       # features per stream
+    io: str                      # storage of x, y, dy, dx: "f32" or "bf16"
+    logits: Tuple                # recipe for the 4 x 4 logits (fp32)
+    hidden: Tuple                # recipe for x
+    upstream: Tuple              # recipe for dL/dy
+    seed: int
+    tol: float = 1e-6
+    max_iter: int = 50
+
+
+MIX_WORKLOADS = {
+    "mix": MixWorkload(
+        key="mix", title="4x4 projection + y = T x, B=16x4096=65,536 tokens, C=4096 bf16 streams, "
+                         "H~N(0,0.5^2)+2I, x~N(0,1), dy~N(0,1)",
+        B=16 * 4096, C=4096, io="bf16", logits=("near_identity", 0.5, 2.0), hidden=("normal", 1.0),
+        upstream=("normal", 1.0), seed=7),
+}
+
+
+def _draw_streams(recipe: Tuple, B: int, C: int, seed: int, io: str) -> np.ndarray:
+    """[B, 4, C] hidden states (fp32, or bf16 bit patterns), drawn 2^22 values at a time."""
+    kind, sigma = recipe
+    if kind != "normal":
+        raise ValueError("unknown stream recipe %r" % (kind,))
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = np.empty((B, 4, C), dtype=np.uint16 if io == "bf16" else np.float32)
+    flat = out.reshape(-1)
+    step = 1 << 22
+    for s in range(0, flat.size, step):
+        e = min(flat.size, s + step)
+        v = (float(sigma) * rng.standard_normal(e - s)).astype(np.float32)
+        flat[s:e] = f32_to_bf16_bits(v) if io == "bf16" else v
+    return out
+
+
+def make_mix(w: MixWorkload, B: Optional[int] = None, C: Optional[int] = None, seed: Optional[int] = None):
+    """(logits [B, 4, 4] fp32, x [B, 4, C], dy [B, 4, C]) for workload w; logits use seed,
+    x seed + 400, dy seed + 500."""
+    B = w.B if B is None else int(B)
+    C = w.C if C is None else int(C)
+    sd = w.seed if seed is None else seed
+    H = _draw(w.logits, B, 4, sd)
+    x = _draw_streams(w.hidden, B, C, sd + 400, w.io)
+    dy = _draw_streams(w.upstream, B, C, sd + 500, w.io)
+    return H, x, dy
+
+
+def mix_bytes_per_token(C: int, io: str, passes: str) -> int:
+    """Algorithmic HBM bytes per token, each input read once, each output written once.
+
+    fwd (birkhoff_fwd_mix): logits + T (16 fp32 each) + dual (4 fp32) + x + y (4C elements each);
+    bwd (birkhoff_mix_bwd): T + dH (16 fp32 each) + x + dy + dx (4C elements each)."""
+    s = 2 if io == "bf16" else 4
+    fwd = 4 * (16 + 16 + 4) + 2 * 4 * C * s
+    bwd = 4 * (16 + 16) + 3 * 4 * C * s
+    if passes == "fwd":
+        return fwd
+    if passes == "bwd":
+        return bwd
+    if passes == "fwd+bwd":
+        return fwd + bwd
+    raise ValueError("unknown passes %r" % (passes,))

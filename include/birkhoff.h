@@ -172,6 +172,37 @@ int birkhoff_eot_fwd(const float* cost, const float* a, const float* b, int shar
 int birkhoff_eot_bwd(const float* T, const float* dT, const float* a, int shared_marginals, float* dcost, int64_t B,
                      int n, int m, float eta, void* stream);
 
+/* ---- The projection's consumer in an mHC layer --------------------------------
+ * The projected matrix is the residual mapping H_res of the layer update
+ * x_{l+1} = H_res x_l + H_post^T F(H_pre x_l) (section 2.1), applied to each
+ * token's n x C hidden matrix x (n streams of C features).  These entry points
+ * fuse that mixing into the projection (forward) and run its backward together
+ * with eq (13) (backward).  n must be 4.  Per token b: logits [B, 4, 4] fp32,
+ * T [B, 4, 4] fp32, dual [B, 4] fp32, dH [B, 4, 4] fp32; x, y, dy, dx
+ * [B, 4, C] row-major (fp32, or bf16 bit patterns for the _bf16 variants), so
+ * element (b, i, c) is at (b*4 + i)*C + c.  C >= 0 must be a multiple of 4
+ * (fp32) or 8 (bf16) so that every row is a whole number of 16-byte chunks;
+ * x, y, dy, dx may be NULL when C == 0.  Arithmetic is fp32; bf16 results are
+ * rounded to nearest, ties to even.  Return codes as above; BIRKHOFF_EINVAL
+ * also covers n != 4, C out of range or not such a multiple. */
+
+/* Forward: T and dual exactly as birkhoff_fwd computes them (bit-identical), and
+ *   y[b] = T[b] x[b]     (y_ic = sum_j T_ij x_jc)
+ * in the same launch; T is not read back from memory for the product. */
+int birkhoff_fwd_mix(const float* logits, const float* x, float* T, float* dual, float* y, int64_t B, int n,
+                     int64_t C, float tol, int max_iter, void* stream);
+int birkhoff_fwd_mix_bf16(const float* logits, const uint16_t* x, float* T, float* dual, uint16_t* y, int64_t B,
+                          int n, int64_t C, float tol, int max_iter, void* stream);
+
+/* Backward of y = T x followed by the projection's backward, for upstream dy:
+ *   dx[b] = T[b]^T dy[b],   dT[b] = dy[b] x[b]^T   (sum over the C columns),
+ *   dH[b] = dL/dlogits from (T[b], dT[b]) by eq (13), as birkhoff_bwd_from_T.
+ * T is the forward's output; dT itself is not stored. */
+int birkhoff_mix_bwd(const float* T, const float* x, const float* dy, float* dx, float* dH, int64_t B, int n,
+                     int64_t C, void* stream);
+int birkhoff_mix_bwd_bf16(const float* T, const uint16_t* x, const uint16_t* dy, uint16_t* dx, float* dH, int64_t B,
+                          int n, int64_t C, void* stream);
+
 /* Static description of a return code (never NULL). */
 const char* birkhoff_strerror(int code);
 

@@ -34,6 +34,7 @@ def test_header_declares_the_entry_points():
     for n in ("birkhoff_fwd", "birkhoff_fwd_ex", "birkhoff_bwd", "sinkhorn_fwd",
               "birkhoff_fwd_bf16", "birkhoff_bwd_bf16", "birkhoff_fwd_bwd", "birkhoff_fwd_bwd_bf16",
               "birkhoff_bwd_from_T", "birkhoff_eot_fwd", "birkhoff_eot_bwd",
+              "birkhoff_fwd_mix", "birkhoff_fwd_mix_bf16", "birkhoff_mix_bwd", "birkhoff_mix_bwd_bf16",
               "birkhoff_strerror", "birkhoff_abi_version"):
         assert n in names
 
@@ -203,6 +204,55 @@ def test_eot_backward_argument_checks(lib):
         assert lib.birkhoff_eot_bwd(ptrs[0], ptrs[1], ptrs[2], 0, ptrs[3], 5, 4, 6, 0.5, None) == EINVAL
         ptrs[k] = Q[k] + 8
         assert lib.birkhoff_eot_bwd(ptrs[0], ptrs[1], ptrs[2], 0, ptrs[3], 5, 4, 6, 0.5, None) == EALIGN
+
+
+# birkhoff_fwd_mix(logits, x, T, dual, y, B, n, C, tol, max_iter, stream)
+@pytest.mark.parametrize("B,n,C,tol,it,want", [
+    (-1, 4, 64, 1e-6, 50, EINVAL),
+    (5, 8, 64, 1e-6, 50, EINVAL),
+    (5, 3, 64, 1e-6, 50, EINVAL),
+    (5, 4, -8, 1e-6, 50, EINVAL),
+    (5, 4, 12, 1e-6, 50, "bf16"),          # a multiple of 4 but not of 8: fp32 only
+    (5, 4, 6, 1e-6, 50, EINVAL),
+    (5, 4, 1 << 29, 1e-6, 50, EINVAL),
+    (1 << 40, 4, 1 << 20, 1e-6, 50, EINVAL),
+    (5, 4, 64, 0.0, 50, EINVAL),
+    (5, 4, 64, math.nan, 50, EINVAL),
+    (5, 4, 64, 1e-6, 0, EINVAL),
+    (0, 4, 64, 1e-6, 50, 0),
+])
+def test_mix_forward_argument_checks(lib, B, n, C, tol, it, want):
+    Q = [A, A + 4096, A + 8192, A + 12288, A + 16384]
+    if want == "bf16":
+        assert lib.birkhoff_fwd_mix_bf16(*Q, B, n, C, tol, it, None) == EINVAL
+        return
+    assert lib.birkhoff_fwd_mix(*Q, B, n, C, tol, it, None) == want
+    assert lib.birkhoff_fwd_mix_bf16(*Q, B, n, C, tol, it, None) == want
+
+
+def test_mix_null_and_misaligned_pointers(lib):
+    """Every call here is rejected on the host (none may reach a launch)."""
+    Q = [A, A + 4096, A + 8192, A + 12288, A + 16384]   # logits, x, T, dual, y
+    for k in range(5):
+        ptrs = list(Q)
+        ptrs[k] = None
+        assert lib.birkhoff_fwd_mix(*ptrs, 9, 4, 64, 1e-6, 50, None) == EINVAL
+        ptrs[k] = Q[k] + 4
+        assert lib.birkhoff_fwd_mix(*ptrs, 9, 4, 64, 1e-6, 50, None) == EALIGN
+        assert lib.birkhoff_fwd_mix_bf16(*ptrs, 9, 4, 64, 1e-6, 50, None) == EALIGN
+    R = [A, A + 4096, A + 8192, A + 12288, A + 16384]   # T, x, dy, dx, dH
+    assert lib.birkhoff_mix_bwd(*R, -1, 4, 64, None) == EINVAL
+    assert lib.birkhoff_mix_bwd(*R, 5, 8, 64, None) == EINVAL
+    assert lib.birkhoff_mix_bwd(*R, 5, 4, 6, None) == EINVAL
+    assert lib.birkhoff_mix_bwd_bf16(*R, 5, 4, 12, None) == EINVAL
+    assert lib.birkhoff_mix_bwd(None, None, None, None, None, 0, 4, 64, None) == 0
+    for k in range(5):
+        ptrs = list(R)
+        ptrs[k] = None
+        assert lib.birkhoff_mix_bwd(*ptrs, 9, 4, 64, None) == EINVAL
+        ptrs[k] = R[k] + 8
+        assert lib.birkhoff_mix_bwd(*ptrs, 9, 4, 64, None) == EALIGN
+        assert lib.birkhoff_mix_bwd_bf16(*ptrs, 9, 4, 64, None) == EALIGN
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
