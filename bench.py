@@ -192,6 +192,122 @@ def eot_report(w, args, dev):
     }
 
 
+def mix_cpu_baseline(w, target_s: float = 10.0):
+    """The float64 oracle for the projection and its consumer (certified projection,
+    y = T x, dx and dT, eq (13)) on a bounded sample of the workload's tokens."""
+    import oracle
+    from birkhoff_projection_amd import workloads as W
+
+    def run(Bs):
+        H, x, dy = W.make_mix(w, B=Bs)
+        H, x, dy = H.astype("float64"), W.decode_f64(x), W.decode_f64(dy)
+        t0 = time.perf_counter()
+        T, _, _ = oracle.project(H)
+        oracle.mix(T, x)
+        _, dT = oracle.mix_bwd(T, x, dy)
+        oracle.bwd(T, dT)
+        return time.perf_counter() - t0
+
+    probe = 256
+    dt = run(probe)
+    Bs = int(min(w.B, max(probe, probe * target_s / max(dt, 1e-6))))
+    dt = run(Bs)
+    return {"value": Bs / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": "the first %d tokens of the same seeded workload (%s), float64: the certified projection, "
+                      "y = T x, dx = T^T dy, dT = dy x^T and the eq (13) backward; %.1f s wall"
+                      % (Bs, "all of it" if Bs == w.B else "a prefix", dt)}
+
+
+def mix_report(w, args, dev):
+    """The projection with its consumer: the step is birkhoff_fwd_mix (project the
+    tokens' logits and mix their hidden states, y = T x) then birkhoff_mix_bwd (dx,
+    and dH through eq (13))."""
+    import torch
+
+    import birkhoff_projection_amd as bp
+    from birkhoff_projection_amd import build as hipbuild
+    from birkhoff_projection_amd import workloads as W
+
+    B, C = w.B, w.C
+    H, x, dy = W.make_mix(w)
+
+    def to_dev(a):
+        t = torch.from_numpy(a).to(dev)
+        return t.view(torch.bfloat16) if w.io == "bf16" else t
+
+    sets = []
+    for _ in range(2):
+        st = {"H": torch.from_numpy(H).to(dev), "x": to_dev(x), "dy": to_dev(dy)}
+        st["y"] = torch.empty_like(st["x"])
+        st["dx"] = torch.empty_like(st["x"])
+        st["T"] = torch.empty((B, 4, 4), dtype=torch.float32, device=dev)
+        st["dual"] = torch.empty((B, 4), dtype=torch.float32, device=dev)
+        st["dH"] = torch.empty((B, 4, 4), dtype=torch.float32, device=dev)
+        sets.append(st)
+    del H, x, dy
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    fwd = bp.birkhoff_fwd_mix_bf16 if w.io == "bf16" else bp.birkhoff_fwd_mix
+    bwd = bp.birkhoff_mix_bwd_bf16 if w.io == "bf16" else bp.birkhoff_mix_bwd
+
+    def run_fwd(s):
+        fwd(s["H"], s["x"], s["T"], s["dual"], s["y"], w.tol, w.max_iter, stream)
+
+    def run_bwd(s):
+        bwd(s["T"], s["x"], s["dy"], s["dx"], s["dH"], stream)
+
+    def step(s):
+        run_fwd(s)
+        run_bwd(s)
+
+    def timed(fn, K):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(K):
+            fn(sets[i % 2])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+
+    for i in range(args.warmup):
+        step(sets[i % 2])
+    torch.cuda.synchronize()
+    K = args.steps
+    ms_step = timed(step, K)
+    fwd_ms = timed(run_fwd, K)
+    bwd_ms = timed(run_bwd, K)
+    # context only: the same product through torch's batched matmul on the stored T
+    def run_torch(s):
+        torch.matmul(s["T"].to(s["x"].dtype), s["x"], out=s["y"])
+    torch_ms = timed(run_torch, max(10, K // 4))
+
+    b_fwd = W.mix_bytes_per_token(C, w.io, "fwd") * B
+    b_bwd = W.mix_bytes_per_token(C, w.io, "bwd") * B
+    kern = {"birkhoff_fwd_mix": (fwd_ms, b_fwd), "birkhoff_mix_bwd": (bwd_ms, b_bwd)}
+    dom = max(kern, key=lambda k: kern[k][0])
+    d_ms, d_bytes = kern[dom]
+    achieved = d_bytes / (d_ms * 1e-3) / 1e9
+    digest = hipbuild.kernel_source_digest()
+    return {
+        "metric": "mHC tokens/sec: 4x4 projection + residual mixing y = T x and its backward (C=%d, %s streams) "
+                  "on 1 MI355X; %% HBM roofline" % (C, w.io),
+        "value": B / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "%s: %s" % (w.key, w.title), "B": B, "C": C, "storage": w.io,
+                   "passes": "fwd+bwd", "tol": w.tol, "max_iter": w.max_iter},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.key, dom, digest),
+                     "algorithmic_bytes_per_launch": d_bytes, "avg_launch_ms": d_ms},
+        "kernels_ms": {"birkhoff_fwd_mix": fwd_ms, "birkhoff_mix_bwd": bwd_ms},
+        "kernels_hbm_frac": {k: v[1] / (v[0] * 1e-3) / 1e9 / HBM_PEAK_GBS for k, v in kern.items()},
+        "torch_matmul_y_ms": torch_ms,
+        "kernel_digest": digest,
+    }
+
+
 def forward_only_report(w, args, dev):
     """A forward-only workload (the hard-conditioning one): the timed step is one
     birkhoff_fwd launch; the fixed 20-sweep Sinkhorn-Knopp kernel is timed on the
@@ -300,9 +416,9 @@ def main() -> int:
     import birkhoff_projection_amd as bp
     from birkhoff_projection_amd import workloads as W
 
-    if args.workload not in W.WORKLOADS and args.workload not in W.EOT_WORKLOADS:
-        print("unknown workload %r (have %s)" % (args.workload, sorted(W.WORKLOADS) + sorted(W.EOT_WORKLOADS)),
-              file=sys.stderr)
+    known = sorted(W.WORKLOADS) + sorted(W.EOT_WORKLOADS) + sorted(W.MIX_WORKLOADS)
+    if args.workload not in known:
+        print("unknown workload %r (have %s)" % (args.workload, known), file=sys.stderr)
         return 2
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -310,6 +426,9 @@ def main() -> int:
     if args.workload in W.EOT_WORKLOADS:
         w = W.EOT_WORKLOADS[args.workload]
         out = eot_report(w, args, dev)
+    elif args.workload in W.MIX_WORKLOADS:
+        w = W.MIX_WORKLOADS[args.workload]
+        out = mix_report(w, args, dev)
     else:
         w = W.WORKLOADS[args.workload]
         out = forward_only_report(w, args, dev) if w.passes == "fwd" else forward_backward_report(w, args, dev)
@@ -322,8 +441,12 @@ def main() -> int:
         out["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": src.numel() * 4}
         del src, dst
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = (eot_cpu_baseline(w, args.cpu_seconds) if args.workload in W.EOT_WORKLOADS
-                               else cpu_baseline(w, args.cpu_seconds))
+        if args.workload in W.EOT_WORKLOADS:
+            out["cpu_baseline"] = eot_cpu_baseline(w, args.cpu_seconds)
+        elif args.workload in W.MIX_WORKLOADS:
+            out["cpu_baseline"] = mix_cpu_baseline(w, args.cpu_seconds)
+        else:
+            out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -4,9 +4,9 @@
 // section 2.1), with H_res the projected 4 x 4 matrix of each token and x the
 // token's n x C hidden matrix (n = 4 streams of C features).
 //
-// Forward (project_mix_kernel): a workgroup takes 64 tokens.  Its first wave
+// Forward (project_mix_kernel): a workgroup takes 4 tokens, one per wave.  Its first wave
 // projects their logits exactly as newton_fwd_kernel does (one matrix per
-// lane) and stores T and the dual; the 64 projections go to LDS, and then all
+// lane) and stores T and the dual; the 4 projections go to LDS, and then all
 // four waves stream the tokens' hidden matrices, token by token, through
 // y_i = sum_j T_ij x_j.  T of the token being streamed is wave-uniform and is
 // held in scalar registers; every lane owns 16-byte column chunks of the four
@@ -17,7 +17,7 @@
 // dT = dy x^T (a reduction over the C columns), then eq (13) turns dT into
 // dL/dH.  The four waves stream x and dy and write dx, accumulating each
 // token's 16 dT partial sums per lane, which one DPP / readlane reduction per
-// entry completes; the 64 dT matrices meet in LDS, and the first wave runs the
+// entry completes; the 4 dT matrices meet in LDS, and the first wave runs the
 // eq (13) backward of implicit_grad for them, one token per lane.
 //
 // The work is HBM-bound: 8 FMAs per element against 2 (fp32) or 1 (bf16)
@@ -30,7 +30,8 @@
 namespace birk {
 namespace mix {
 
-constexpr int kTokens = 64;    // tokens per workgroup (one projecting wave)
+constexpr int kTokens = 4;     // tokens per workgroup (one per wave): small, so that the grid has many
+                               // workgroups and the last round of them is short
 constexpr int kUnroll = 4;     // column chunks per lane in flight per row
 constexpr int kTs = 17;        // LDS stride of a token's 16 entries (odd: no bank conflicts)
 
@@ -139,7 +140,7 @@ __device__ __forceinline__ void mix_token(const float (&t)[16], const uint4* __r
     }
 }
 
-// Projection of 64 tokens' 4 x 4 logits (first wave) and the mixing of their
+// Projection of the workgroup's tokens' 4 x 4 logits (first wave) and the mixing of their
 // hidden matrices (all waves).  Q = 16-byte chunks per hidden row (C / V).
 template <typename XT>
 __global__ void __launch_bounds__(kBlock)
@@ -151,12 +152,13 @@ project_mix_kernel(const float* __restrict__ logits, const XT* __restrict__ x, f
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t first = (int64_t)blockIdx.x * kTokens;
     if (wave == 0) {
-        const Gm geo(B, first);
+        const Gm geo(B, first, kTokens);
         float T[16], yv[3], res;
         newton_solve<4, float>(geo, tile, logits, tol, max_iter, T, yv, res);
         store_forward<4, float>(geo, tile, Tout, dual, T, yv);
+        if (lane < kTokens)
 #pragma unroll
-        for (int k = 0; k < 16; ++k) Ts[lane * kTs + k] = T[k];
+            for (int k = 0; k < 16; ++k) Ts[lane * kTs + k] = T[k];
     }
     __syncthreads();
     const int64_t left = B - first;

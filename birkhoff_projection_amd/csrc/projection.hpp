@@ -418,14 +418,14 @@ struct Geometry {
         const int64_t left = B * R - base;
         nvalid = __builtin_amdgcn_readfirstlane(left <= 0 ? 0 : left >= 64 ? 64 : (int)left);
     }
-    // one wave whose first item is `first` (wave-uniform), for kernels where a
-    // single wave of the workgroup projects
-    __device__ __forceinline__ Geometry(int64_t B, int64_t first) {
+    // one wave whose first item is `first` (wave-uniform) and which takes at most
+    // `span` <= 64 items, for kernels where a single wave of the workgroup projects
+    __device__ __forceinline__ Geometry(int64_t B, int64_t first, int span) {
         lane = threadIdx.x & 63;
         wave = 0;
         base = first;
         const int64_t left = B * R - base;
-        nvalid = __builtin_amdgcn_readfirstlane(left <= 0 ? 0 : left >= 64 ? 64 : (int)left);
+        nvalid = __builtin_amdgcn_readfirstlane(left <= 0 ? 0 : left >= span ? span : (int)left);
     }
     __device__ __forceinline__ bool valid() const { return lane < nvalid; }
     __device__ __forceinline__ int half() const { return lane & (R - 1); }            // which rows of the matrix

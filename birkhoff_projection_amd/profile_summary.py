@@ -33,7 +33,8 @@ ROOT = pathlib.Path(__file__).resolve().parent.parent
 ENTRY = (("newton_fwd_kernel", "birkhoff_fwd"), ("implicit_bwd_from_T_kernel", "birkhoff_bwd_from_T"),
          ("implicit_bwd_kernel", "birkhoff_bwd"),
          ("sinkhorn_kernel", "sinkhorn_fwd"), ("fused_fwd_bwd_kernel", "birkhoff_fwd_bwd"),
-         ("eot_fwd_kernel", "birkhoff_eot_fwd"), ("eot_bwd_kernel", "birkhoff_eot_bwd"))
+         ("eot_fwd_kernel", "birkhoff_eot_fwd"), ("eot_bwd_kernel", "birkhoff_eot_bwd"),
+         ("project_mix_kernel", "birkhoff_fwd_mix"), ("mix_bwd_kernel", "birkhoff_mix_bwd"))
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
