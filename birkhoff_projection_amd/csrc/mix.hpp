@@ -7,8 +7,9 @@
 // Forward (project_mix_kernel): a workgroup takes 4 tokens, one per wave.  Its first wave
 // projects their logits exactly as newton_fwd_kernel does (one matrix per
 // lane) and stores T and the dual; the 4 projections go to LDS, and then all
-// four waves stream the tokens' hidden matrices, token by token, through
-// y_i = sum_j T_ij x_j.  T of the token being streamed is wave-uniform and is
+// four waves stream the tokens' hidden matrices, one token each, through
+// y_i = sum_j T_ij x_j (each wave's first loads are issued before the
+// projection, so they are in flight while it runs).  T of the token being streamed is wave-uniform and is
 // held in scalar registers; every lane owns 16-byte column chunks of the four
 // rows, so each access instruction is a coalesced 1 KiB.  The epilogue never
 // writes T to HBM and reads it back: the stored T is for the backward.
@@ -91,52 +92,61 @@ __device__ __forceinline__ float wave_sum(float v) {
     return (r0 + r1) + (r2 + r3);
 }
 
-// y_i = sum_j T_ij x_j for one token: rows of Q 16-byte chunks at xr + j*Q and
-// yr + i*Q; lane l handles chunks l, l + 64, ...  T is wave-uniform.
+// The loads of one batch of a token's columns: chunks q + 64u (u < kUnroll) of
+// its four rows, all issued before any is used.
+__device__ __forceinline__ void load_batch(const uint4* __restrict__ xr, int64_t Q, int64_t q,
+                                           uint4 (&w)[kUnroll][4]) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[u][j] = stream_load(xr + j * Q + q + 64 * u);
+}
+
+// y_i = sum_j T_ij x_j for the chunk whose four row pieces are w, stored at
+// chunk q of each output row.
 template <typename XT>
-__device__ __forceinline__ void mix_token(const float (&t)[16], const uint4* __restrict__ xr, uint4* __restrict__ yr,
-                                          int64_t Q, int lane) {
+__device__ __forceinline__ void mix_chunk(const float (&t)[16], const uint4 (&w)[4], uint4* __restrict__ yr,
+                                          int64_t Q, int64_t q) {
     using Vx = Vec<XT>;
     constexpr int V = Vx::V;
+    float xv[4][V];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Vx::decode(w[j], xv[j]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float o[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e)
+            o[e] = fmaf(t[4 * i + 3], xv[3][e], fmaf(t[4 * i + 2], xv[2][e],
+                        fmaf(t[4 * i + 1], xv[1][e], t[4 * i] * xv[0][e])));
+        stream_store(yr + i * Q + q, Vx::encode(o));
+    }
+}
+
+// y_i = sum_j T_ij x_j for one token: rows of Q 16-byte chunks at xr + j*Q and
+// yr + i*Q; lane l handles chunks l, l + 64, ...  T is wave-uniform.  When
+// `pre` is set (per lane, only if lane + 64 (kUnroll - 1) < Q), the batch at
+// q = lane has already been loaded into w0.
+template <typename XT>
+__device__ __forceinline__ void mix_token(const float (&t)[16], const uint4* __restrict__ xr, uint4* __restrict__ yr,
+                                          int64_t Q, int lane, bool pre, const uint4 (&w0)[kUnroll][4]) {
     int64_t q = lane;
+    if (pre) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) mix_chunk<XT>(t, w0[u], yr, Q, q + 64 * u);
+        q += 64 * kUnroll;
+    }
     for (; q + 64 * (kUnroll - 1) < Q; q += 64 * kUnroll) {
         uint4 w[kUnroll][4];
+        load_batch(xr, Q, q, w);
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) w[u][j] = stream_load(xr + j * Q + q + 64 * u);
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            float xv[4][V];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) Vx::decode(w[u][j], xv[j]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float o[V];
-#pragma unroll
-                for (int e = 0; e < V; ++e)
-                    o[e] = fmaf(t[4 * i + 3], xv[3][e], fmaf(t[4 * i + 2], xv[2][e],
-                                fmaf(t[4 * i + 1], xv[1][e], t[4 * i] * xv[0][e])));
-                stream_store(yr + i * Q + q + 64 * u, Vx::encode(o));
-            }
-        }
+        for (int u = 0; u < kUnroll; ++u) mix_chunk<XT>(t, w[u], yr, Q, q + 64 * u);
     }
     for (; q < Q; q += 64) {
         uint4 w[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) w[j] = stream_load(xr + j * Q + q);
-        float xv[4][V];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) Vx::decode(w[j], xv[j]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float o[V];
-#pragma unroll
-            for (int e = 0; e < V; ++e)
-                o[e] = fmaf(t[4 * i + 3], xv[3][e], fmaf(t[4 * i + 2], xv[2][e],
-                            fmaf(t[4 * i + 1], xv[1][e], t[4 * i] * xv[0][e])));
-            stream_store(yr + i * Q + q, Vx::encode(o));
-        }
+        mix_chunk<XT>(t, w, yr, Q, q);
     }
 }
 
@@ -147,10 +157,20 @@ __global__ void __launch_bounds__(kBlock)
 project_mix_kernel(const float* __restrict__ logits, const XT* __restrict__ x, float* __restrict__ Tout,
                    float* __restrict__ dual, XT* __restrict__ y, int64_t B, int64_t Q, float tol, int max_iter) {
     using Gm = Geometry<4, float>;
+    static_assert(kTokens == kWaves, "one token per wave");
     __shared__ uint4 tile[Gm::Tile::kLdsChunks];
     __shared__ float Ts[kTokens * kTs];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t first = (int64_t)blockIdx.x * kTokens;
+    const int64_t left = B - first;
+    const int ntok = left >= kTokens ? kTokens : (int)left;
+    // this wave's token: its first batch of hidden-state loads is issued now, so
+    // that it is in flight while the first wave projects
+    const bool mine = wave < ntok;
+    const bool pre = mine && lane + 64 * (kUnroll - 1) < Q;   // per lane: every chunk of the batch exists
+    const int64_t row0 = (first + wave) * 4 * Q;
+    uint4 w0[kUnroll][4];
+    if (pre) load_batch(reinterpret_cast<const uint4*>(x) + row0, Q, lane, w0);
     if (wave == 0) {
         const Gm geo(B, first, kTokens);
         float T[16], yv[3], res;
@@ -161,14 +181,12 @@ project_mix_kernel(const float* __restrict__ logits, const XT* __restrict__ x, f
             for (int k = 0; k < 16; ++k) Ts[lane * kTs + k] = T[k];
     }
     __syncthreads();
-    const int64_t left = B - first;
-    const int ntok = left >= kTokens ? kTokens : (int)left;
-    for (int t = wave; t < ntok; t += kWaves) {
+    if (mine) {
         float tm[16];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) tm[k] = uniform(Ts[t * kTs + k]);
-        const int64_t row0 = (first + t) * 4 * Q;
-        mix_token<XT>(tm, reinterpret_cast<const uint4*>(x) + row0, reinterpret_cast<uint4*>(y) + row0, Q, lane);
+        for (int k = 0; k < 16; ++k) tm[k] = uniform(Ts[wave * kTs + k]);
+        mix_token<XT>(tm, reinterpret_cast<const uint4*>(x) + row0, reinterpret_cast<uint4*>(y) + row0, Q, lane, pre,
+                      w0);
     }
 }
 
