@@ -197,29 +197,29 @@ __device__ __forceinline__ void mix_token_bwd(const float (&t)[16], const uint4*
                                               int lane, float (&acc)[16]) {
     using Vx = Vec<XT>;
     constexpr int V = Vx::V;
+    // element by element (few values live at once): dT partial sums and the
+    // four dx outputs of each column of the chunk
     auto chunk = [&](const uint4 (&wx)[4], const uint4 (&wd)[4], int64_t qq) {
-        float xv[4][V], dv[4][V];
+        float xv[4][V], dv[4][V], o[4][V];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             Vx::decode(wx[j], xv[j]);
             Vx::decode(wd[j], dv[j]);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int e = 0; e < V; ++e) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[4 * i + j] = fmaf(dv[i][e], xv[j][e], acc[4 * i + j]);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int e = 0; e < V; ++e) acc[4 * i + j] = fmaf(dv[i][e], xv[j][e], acc[4 * i + j]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float o[V];
-#pragma unroll
-            for (int e = 0; e < V; ++e)
-                o[e] = fmaf(t[12 + j], dv[3][e], fmaf(t[8 + j], dv[2][e], fmaf(t[4 + j], dv[1][e], t[j] * dv[0][e])));
-            stream_store(dxr + j * Q + qq, Vx::encode(o));
+                o[j][e] = fmaf(t[12 + j], dv[3][e], fmaf(t[8 + j], dv[2][e], fmaf(t[4 + j], dv[1][e], t[j] * dv[0][e])));
         }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) stream_store(dxr + j * Q + qq, Vx::encode(o[j]));
     };
-    constexpr int U = kUnroll / 2;   // two input streams
+    constexpr int U = 1;   // two input streams: 8 chunks in flight per lane
     int64_t q = lane;
     for (; q + 64 * (U - 1) < Q; q += 64 * U) {
         uint4 wx[U][4], wd[U][4];
