@@ -246,20 +246,22 @@ __device__ __forceinline__ float log1p_minus_x(float q, float l1p) {
 //     = sum_j [c_j (e^{s_j} - 1 - s_j) + g_j s_j] + sum_i a_i [log(1 + q_i) - q_i],
 // so that its sign stays reliable in fp32 down to tiny steps.  Returns the
 // change; e, r and the column sums ct of T' = diag(a) S' are returned for
-// accept_trial and the gradient test.
+// accept_trial and the gradient test, and `noise` is 2^-21 times the sum of the
+// terms' magnitudes (below it fp32 cannot resolve the change's sign).
 template <int N, int M>
 __device__ __forceinline__ float trial_point(const float (&S)[N * M], const float (&a)[N], const float (&c)[M],
                                              const float (&g)[M - 1], const float (&s)[M - 1], float (&e)[M - 1],
-                                             float (&r)[N], float (&ct)[M]) {
+                                             float (&r)[N], float (&ct)[M], float& noise) {
     constexpr int K1 = M - 1;
     float em[K1];
-    float df = 0.0f;
+    float df = 0.0f, mag = 0.0f;
 #pragma unroll
     for (int j = 0; j < K1; ++j) {
         e[j] = ex2(s[j] * kLog2e);
         float xm;
         expm1_pair(s[j], e[j], em[j], xm);
         df = fmaf(c[j], xm, fmaf(g[j], s[j], df));
+        mag += fabsf(c[j] * xm) + fabsf(g[j] * s[j]);
     }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
@@ -274,12 +276,15 @@ __device__ __forceinline__ float trial_point(const float (&S)[N * M], const floa
             rs += u[j];
         }
         r[i] = rcp(rs);
-        df = fmaf(a[i], log1p_minus_x(q, lg2(rs) * kLn2), df);
+        const float lq = a[i] * log1p_minus_x(q, lg2(rs) * kLn2);
+        df += lq;
+        mag += fabsf(lq);
         const float ar = a[i] * r[i];
 #pragma unroll
         for (int j = 0; j < K1; ++j) ct[j] = (i == 0) ? u[j] * ar : fmaf(u[j], ar, ct[j]);
         ct[K1] = (i == 0) ? S[i * M + K1] * ar : fmaf(S[i * M + K1], ar, ct[K1]);
     }
+    noise = mag * 0x1.0p-21f;
     return df;
 }
 
@@ -360,7 +365,7 @@ struct Lanes {
     __device__ __forceinline__ int64_t problem() const { return base + lane; }
 };
 
-// Forward: Newton on the reduced dual (eq 8) from z = log(b / b_{m-1}) until the column
+// Forward: Newton on the reduced dual (eq 8) from one Sinkhorn sweep until the column
 // marginals are met to `tol` (absolute) or `max_iter` updates; rows are met by
 // construction.  Step sizes 1, 1/2, 1/10, 1/20, 1/100, the first that lowers
 // both the objective and the gradient norm is taken; otherwise one Sinkhorn
@@ -384,9 +389,12 @@ eot_fwd_kernel(const float* __restrict__ cost, const float* __restrict__ a_in, c
     float a[N], b[M];
     load_marginal<N>(a_in, shared, ln.base, ln.nvalid, lds, ln.lane, a);
     load_marginal<M>(b_in, shared, ln.base, ln.nvalid, lds, ln.lane, b);
-    // start at z = log(b / b_{m-1}) (base 2 here): the optimum when the cost is
-    // constant (plan a b^T / sum(b)), and z = 0 when b = 1 as for the Birkhoff
-    // projection; lanes past the end (b = 0) start at 0
+    // start: one Sinkhorn-Knopp sweep (eqs 5-6) from z = log(b / b_{m-1}) (base 2
+    // here), i.e. the rows normalised at that z and then the columns scaled to b:
+    // z_j += log(b_j / c_j) - log(b_{m-1} / c_{m-1}).  It is the optimum when the
+    // cost is constant (plan a b^T / sum(b)) and the Birkhoff kernels' start when
+    // a = b = 1.  The sweep is skipped if a column sum is 0 or not finite; lanes
+    // past the end (b = 0) start at 0.
     float S[N * M], y[K1], c[M];
     {
         const float lbm = ln.valid() ? lg2(b[K1]) : 0.0f;
@@ -397,6 +405,31 @@ eot_fwd_kernel(const float* __restrict__ cost, const float* __restrict__ a_in, c
 #pragma unroll
         for (int k = 0; k < N * M; ++k) L[k] *= lscale;
         softmax_rows<M, N>(L, y, S);
+    }
+    col_sums<N, M>(S, a, c);
+    {
+        // the sweep's column step: S_ij <- S_ij b_j / c_j, rows normalised again
+        bool ok = ln.valid();
+#pragma unroll
+        for (int j = 0; j < M; ++j) ok = ok && c[j] > 1.17549435e-38f && c[j] < 3.0e38f;
+        float f[M];
+#pragma unroll
+        for (int j = 0; j < M; ++j) f[j] = ok ? b[j] * rcp(c[j]) : 1.0f;
+        const float rf = rcp(f[K1]);
+#pragma unroll
+        for (int j = 0; j < K1; ++j) y[j] = ok ? y[j] + lg2(f[j] * rf) : y[j];
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            float rs = 0.0f;
+#pragma unroll
+            for (int j = 0; j < M; ++j) {
+                S[i * M + j] *= f[j];
+                rs += S[i * M + j];
+            }
+            const float r = rcp(rs);
+#pragma unroll
+            for (int j = 0; j < M; ++j) S[i * M + j] *= r;
+        }
     }
     col_sums<N, M>(S, a, c);
     float res = ln.valid() ? col_residual<M>(c, b) : 0.0f;
@@ -424,11 +457,12 @@ eot_fwd_kernel(const float* __restrict__ cost, const float* __restrict__ a_in, c
                 float s[K1], e[K1], rr[N], ct[M];
 #pragma unroll
                 for (int j = 0; j < K1; ++j) s[j] = gam * d[j];
-                const float df = trial_point<N, M>(S, a, c, g, s, e, rr, ct);
+                float noise;
+                const float df = trial_point<N, M>(S, a, c, g, s, e, rr, ct, noise);
                 float gt2 = (ct[0] - b[0]) * (ct[0] - b[0]);
 #pragma unroll
                 for (int j = 1; j < K1; ++j) gt2 = fmaf(ct[j] - b[j], ct[j] - b[j], gt2);
-                if (df < 0.0f && gt2 < gn2) {
+                if (df < noise && gt2 < gn2) {
 #pragma unroll
                     for (int j = 0; j < K1; ++j) y[j] = fmaf(s[j], kLog2e, y[j]);
                     accept_trial<N, M>(S, e, rr);

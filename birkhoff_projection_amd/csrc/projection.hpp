@@ -286,10 +286,13 @@ struct SpdSolve<4> {
 // Otherwise (|q| >= 1/16) the logarithms of the row sums themselves are added.
 // T' itself is not formed: the column sums ct of T' (for the gradient
 // test) are accumulated row by row, and e, r are returned so that an accepted
-// trial is applied to T in place by accept_trial.  Returns f(x + s) - f(x).
+// trial is applied to T in place by accept_trial.  Returns f(x + s) - f(x);
+// `noise` receives 2^-21 times the magnitude of the two terms it is the
+// difference of, the level below which fp32 cannot resolve its sign.
 template <int N>
 __device__ __forceinline__ float trial_point(const float (&T)[Split<N>::K * N], const float (&s)[N - 1],
-                                             float (&e)[N - 1], float (&r)[Split<N>::K], float (&ct)[N]) {
+                                             float (&e)[N - 1], float (&r)[Split<N>::K], float (&ct)[N],
+                                             float& noise) {
     constexpr int M = N - 1, K = Split<N>::K;
     using P = Pair<Split<N>::R>;
     float em[M];
@@ -327,7 +330,9 @@ __device__ __forceinline__ float trial_point(const float (&T)[Split<N>::K * N], 
     }
 #pragma unroll
     for (int j = 0; j < N; ++j) ct[j] = P::sum(ct[j]);
-    return (fabsf(q) < 0.0625f ? log1p_series(q) : P::sum(lsum) * kLn2) - ssum;
+    const float l = fabsf(q) < 0.0625f ? log1p_series(q) : P::sum(lsum) * kLn2;
+    noise = (fabsf(l) + fabsf(ssum)) * 0x1.0p-21f;
+    return l - ssum;
 }
 
 template <int N>
@@ -490,7 +495,8 @@ __device__ __forceinline__ void load_own(const IO* __restrict__ p, int64_t item,
 // Forward: Newton on the reduced dual (eq 8).
 // ---------------------------------------------------------------------------
 
-// Loads the wave's logits, evaluates T at x^(0) = 0 and runs Newton's method to
+// Loads the wave's logits, evaluates T at the start x^(0) (one Sinkhorn sweep
+// from beta = 0) and runs Newton's method to
 // column-sum residual <= tol or max_iter updates.  On return T is the lane's
 // rows of the last iterate, y the dual (base-2 units, y_{N-1} = 0 implied),
 // res its residual; returns the number of updates.  The logits are needed
@@ -505,8 +511,6 @@ __device__ __forceinline__ int newton_solve(const Geometry<N, IO>& geo, uint4* l
     using G = Geometry<N, IO>;
     // the iteration works on locals, copied out at the end (keeps the loop in registers)
     float T[K * N], y[M], c[N], res;
-#pragma unroll
-    for (int j = 0; j < M; ++j) y[j] = 0.0f;   // x^(0) = 0
     {
         float L[K * N];
         uint4 w[G::C];
@@ -519,6 +523,34 @@ __device__ __forceinline__ int newton_solve(const Geometry<N, IO>& geo, uint4* l
     // optionally start copying another tile of the wave (dL/dT) into the now
     // free LDS region, to be read after the iteration
     if constexpr (kPrefetch) G::Tile::prefetch(geo.chunks(prefetch_src), geo.nvalid * G::C, lds, geo.lane);
+    // start: the dual after one Sinkhorn-Knopp sweep from v = 1 -- the rows of
+    // exp(H) normalised (T at beta = 0 above), then its columns scaled to sum to
+    // one and the rows normalised again, which is T at
+    // beta_j = log c_{n-1} - log c_j; kept at beta = 0 if a column sum is 0 or
+    // not finite
+    col_sums<N>(T, c);
+    {
+        bool ok = true;
+#pragma unroll
+        for (int j = 0; j < N; ++j) ok = ok && c[j] > 1.17549435e-38f && c[j] < 3.0e38f;
+        float rc[N];
+#pragma unroll
+        for (int j = 0; j < N; ++j) rc[j] = ok ? rcp(c[j]) : 1.0f;
+#pragma unroll
+        for (int j = 0; j < M; ++j) y[j] = ok ? lg2(c[N - 1] * rc[j]) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+            float rs = 0.0f;
+#pragma unroll
+            for (int j = 0; j < N; ++j) {
+                T[i * N + j] *= rc[j];
+                rs += T[i * N + j];
+            }
+            const float r = rcp(rs);
+#pragma unroll
+            for (int j = 0; j < N; ++j) T[i * N + j] *= r;
+        }
+    }
     col_sums<N>(T, c);
     res = geo.valid() ? col_residual<N>(c) : 0.0f;   // lanes past the end are done
     int it = 0;
@@ -545,11 +577,14 @@ __device__ __forceinline__ int newton_solve(const Geometry<N, IO>& geo, uint4* l
                 float s[M], e[M], rr[K], ct[N];
 #pragma unroll
                 for (int j = 0; j < M; ++j) s[j] = gam * d[j];
-                const float df = trial_point<N>(T, s, e, rr, ct);
+                float noise;
+                const float df = trial_point<N>(T, s, e, rr, ct, noise);
                 float gt2 = (ct[0] - 1.0f) * (ct[0] - 1.0f);
 #pragma unroll
                 for (int j = 1; j < M; ++j) gt2 = fmaf(ct[j] - 1.0f, ct[j] - 1.0f, gt2);
-                if (df < 0.0f && gt2 < gn2) {
+                // the objective must not increase beyond what fp32 can resolve, and
+                // the gradient norm must decrease
+                if (df < noise && gt2 < gn2) {
 #pragma unroll
                     for (int j = 0; j < M; ++j) y[j] = fmaf(s[j], kLog2e, y[j]);
                     accept_trial<N>(T, e, rr);

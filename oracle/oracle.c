@@ -252,7 +252,11 @@ static double colsum_residual(const double *c, int n)
     return r;
 }
 
-/* Newton's method for min_x f(x), x = beta_{-n} (eq 8), from x = 0.
+/* Newton's method for min_x f(x), x = beta_{-n} (eq 8), from the dual after one
+ * Sinkhorn-Knopp sweep from beta = 0 (the pages leave x^(0) open): the rows of
+ * exp(H) normalised (T at beta = 0), then its columns scaled to sum to one,
+ *   beta_j = -log c_j + log c_n,  c = column sums of T at beta = 0,
+ * which is not counted as an update (kept at 0 when a column sum underflows).
  *   gradient  g = c_{-n} - 1                           (eq 9, a = b = 1)
  *   Hessian   diag(c_{-n}) - T_{-n}^T T_{-n}           (eq 9, eta = 1)
  *   step      x+ = x + gamma d,  d = -Hess^{-1} g
@@ -272,12 +276,18 @@ static int newton_one(const double *H, int n, double tol, int max_iter,
 {
     static const double steps[5] = {1.0, 0.5, 0.1, 0.05, 0.01};
     const int m = n - 1;
-    double beta[ORACLE_NMAX], c[ORACLE_NMAX], g[ORACLE_NMAX], d[ORACLE_NMAX];
+    double beta[ORACLE_NMAX] = {0}, c[ORACLE_NMAX] = {0}, g[ORACLE_NMAX], d[ORACLE_NMAX];
     double hess[ORACLE_NMAX * ORACLE_NMAX];
     double bt[ORACLE_NMAX], Tt[ORACLE_NMAX * ORACLE_NMAX], ct[ORACLE_NMAX];
     double alpha[ORACLE_NMAX];
     for (int j = 0; j < n; ++j) beta[j] = 0.0;
     eval_T(H, n, beta, T, c);
+    int ok = 1;
+    for (int j = 0; j < n; ++j) ok = ok && c[j] > 0.0 && isfinite(c[j]);
+    if (ok) {
+        for (int j = 0; j < n; ++j) beta[j] = -log(c[j]) + log(c[n - 1]);
+        eval_T(H, n, beta, T, c);
+    }
     int it = 0, conv = 0;
     for (;;) {
         double res = colsum_residual(c, n);
@@ -487,10 +497,13 @@ static void eot_eval_T(const double *M, const double *a, int n, int m, double et
     }
 }
 
-/* Newton's method on the reduced dual (eq 8), from x^(0) = eta (log b_{-m} - log b_m)
- * (the pages leave x^(0) open; this start is x = 0 when b = 1, as in the
- * Birkhoff case, and is already the optimum when the cost is constant, whose
- * plan is a b^T / sum(b)):
+/* Newton's method on the reduced dual (eq 8), from the dual after one
+ * Sinkhorn-Knopp sweep (eqs 5-7) from beta = eta log(b / b_m) (the pages leave
+ * x^(0) open; this reduces to newton_one's start when a = b = 1 and eta = 1, and
+ * is already the optimum when the cost is constant, whose plan is
+ * a b^T / sum(b)): with c the column sums of T at that beta,
+ *   beta_j <- beta_j + eta (log(b_j / c_j) - log(b_m / c_m)),
+ * not counted as an update (skipped when a column sum underflows):
  *   gradient  g = c_{-m} - b_{-m}                                   (eq 9)
  *   Hessian   eta^-1 [diag(c_{-m}) - T_{-m}^T diag(a)^-1 T_{-m}]    (eq 9)
  * with the step-size rule and Sinkhorn fallback of [B] section 2.2, as in
@@ -504,12 +517,19 @@ static int eot_newton_one(const double *M, const double *a, const double *b, int
 {
     static const double steps[5] = {1.0, 0.5, 0.1, 0.05, 0.01};
     const int k1 = m - 1;
-    double beta[ORACLE_NMAX], c[ORACLE_NMAX], g[ORACLE_NMAX], d[ORACLE_NMAX];
+    double beta[ORACLE_NMAX] = {0}, c[ORACLE_NMAX] = {0}, g[ORACLE_NMAX], d[ORACLE_NMAX];
     double hess[ORACLE_NMAX * ORACLE_NMAX];
     double bt[ORACLE_NMAX], Tt[ORACLE_NMAX * ORACLE_NMAX], ct[ORACLE_NMAX];
     double alpha[ORACLE_NMAX];
     for (int j = 0; j < m; ++j) beta[j] = eta * (log(b[j]) - log(b[m - 1]));
     eot_eval_T(M, a, n, m, eta, beta, T, c);
+    int ok = 1;
+    for (int j = 0; j < m; ++j) ok = ok && c[j] > 0.0 && isfinite(c[j]);
+    if (ok) {
+        const double cm = log(b[m - 1] / c[m - 1]);
+        for (int j = 0; j < m; ++j) beta[j] += eta * (log(b[j] / c[j]) - cm);
+        eot_eval_T(M, a, n, m, eta, beta, T, c);
+    }
     int it = 0, conv = 0;
     for (;;) {
         double res = 0.0;

@@ -231,6 +231,32 @@ def test_reduced_dual_with_library_minimiser(n):
         np.testing.assert_allclose(b_or[0], beta, rtol=0, atol=1e-6)
 
 
+@pytest.mark.parametrize("n", [3, 4, 8])
+def test_first_newton_step_from_the_sweep_start(n):
+    """One Newton update (the full step, on mild inputs) from the start x0 = the dual
+    after one Sinkhorn sweep from v = 1, i.e. beta_j = -log c_j + log c_n with c the
+    column sums of the row-normalised exp(H): x1 = x0 - H^{-1} g with g and H the
+    finite-difference gradient and Hessian of eq (8) at x0."""
+    rng = np.random.default_rng(50 + n)
+    H = 0.3 * rng.standard_normal((5, n, n))
+    _, beta1, _ = oracle.newton(H, 1e-13, 1)
+    for q in range(5):
+        Hq = H[q]
+
+        def f(x):
+            beta = np.append(x, 0.0)
+            return n + logsumexp(Hq + beta[None, :], axis=1).sum() - beta.sum()
+
+        c = softmax(Hq, axis=1).sum(axis=0)
+        x0 = -np.log(c[:-1]) + np.log(c[-1])
+        k, h = n - 1, 1e-4
+        E = np.eye(k) * h
+        g = np.array([(f(x0 + E[i]) - f(x0 - E[i])) / (2 * h) for i in range(k)])
+        Hs = np.array([[(f(x0 + E[i] + E[j]) - f(x0 + E[i] - E[j]) - f(x0 - E[i] + E[j]) + f(x0 - E[i] - E[j]))
+                        / (4 * h * h) for j in range(k)] for i in range(k)])
+        np.testing.assert_allclose(beta1[q, :-1], x0 - np.linalg.solve(Hs, g), rtol=1e-5, atol=1e-7)
+
+
 @pytest.mark.parametrize("n,sigma", [(3, 1.0), (4, 1.0), (4, 3.0), (5, 2.0), (8, 1.0)])
 def test_newton_and_sinkhorn_agree(n, sigma):
     """Two algorithms, one answer: Newton on eq (8) and Sinkhorn-Knopp eq (2)."""
