@@ -17,7 +17,10 @@ cache.  The timed region is `--steps` back-to-back steps between two HIP events
 on the stream the kernels run on; `value` is B / (time per step).
 
 The roofline figure is for the kernel with the longer average launch time
-(the fused kernel is the only one of its step).  Each separate kernel's
+(the fused kernel is the only one of its step).  It is an HBM figure unless the
+committed counters for the same kernel sources show the vector ALUs busier
+than HBM; then the kernel is reported as ALU-bound, against the VALU issue peak
+(see roofline()).  Each separate kernel's
 average launch time is measured as `--steps` back-to-back launches of that
 kernel alone (alternating the two sets) between two HIP events on the same
 stream -- events between the two kernels of a step would themselves add gaps.
@@ -47,16 +50,43 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak, GB/s
 METRIC = "4x4 Birkhoff projections/sec (fwd+bwd, fp32) on 1 MI355X; % HBM roofline"
 
 
+VALU_PEAK = 256 * 4 * 16 * 2.4e9   # lane-instructions/s: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+
+
+def _profile(workload: str, digest: str):
+    p = ROOT / "profiles" / ("traffic_%s.json" % workload)
+    if not p.exists():
+        return {}
+    d = json.loads(p.read_text())
+    return d if d.get("kernel_digest") == digest else {}
+
+
 def measured_traffic(workload: str, kernel: str, digest: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel sources (else None)."""
-    p = ROOT / "profiles" / ("traffic_%s.json" % workload)
-    if not p.exists():
-        return None
-    d = json.loads(p.read_text())
-    if d.get("kernel_digest") != digest or kernel not in d.get("bytes_per_launch", {}):
-        return None
-    return d["bytes_per_launch"][kernel]
+    return _profile(workload, digest).get("bytes_per_launch", {}).get(kernel)
+
+
+def roofline(workload: str, kernel: str, nbytes: float, ms: float, digest: str) -> dict:
+    """The dominant kernel against its bound.  HBM: algorithmic bytes per launch
+    over the launch time, against 8 TB/s.  When the committed counters (same
+    kernel sources) show the vector ALUs busier than HBM, the kernel is reported
+    as ALU-bound: VALU lane-instructions per launch (SQ_INSTS_VALU x 64) over the
+    launch time, against the issue peak of 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+    = 39.3e12 lane-instructions/s; the HBM figures stay alongside."""
+    hbm = nbytes / (ms * 1e-3) / 1e9
+    out = {"bound": "hbm", "kernel": kernel, "achieved": hbm, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": hbm / HBM_PEAK_GBS, "traffic": measured_traffic(workload, kernel, digest),
+           "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": ms}
+    valu = _profile(workload, digest).get("valu_insts_per_launch", {}).get(kernel)
+    if valu is not None:
+        rate = valu * 64 / (ms * 1e-3)
+        out["valu_frac"] = rate / VALU_PEAK
+        if rate / VALU_PEAK > hbm / HBM_PEAK_GBS:
+            out.update({"bound": "alu", "achieved": rate / 1e12, "peak": VALU_PEAK / 1e12,
+                        "unit": "T lane-instr/s", "frac": rate / VALU_PEAK, "hbm_GBs": hbm,
+                        "hbm_frac": hbm / HBM_PEAK_GBS})
+    return out
 
 
 def cpu_baseline(w, target_s: float = 10.0):
@@ -65,12 +95,15 @@ def cpu_baseline(w, target_s: float = 10.0):
     import oracle
     from birkhoff_projection_amd import workloads as W
 
+    fwd_only = w.upstream is None
+
     def run(Bs):
         H = W.decode_f64(W.make_logits(w, B=Bs))
-        G = W.decode_f64(W.make_upstream(w, B=Bs))
+        G = None if fwd_only else W.decode_f64(W.make_upstream(w, B=Bs))
         t0 = time.perf_counter()
         T, _, _ = oracle.project(H, sk_cap=w.sk_cap)
-        oracle.bwd(T, G)
+        if not fwd_only:
+            oracle.bwd(T, G)
         return time.perf_counter() - t0
 
     probe = 8192
@@ -79,8 +112,9 @@ def cpu_baseline(w, target_s: float = 10.0):
     dt = run(Bs)
     return {"value": Bs / dt, "unit": "projections/s", "cores": oracle.threads(), "kind": "oracle",
             "sample": "the first %d matrices of the same seeded workload (%s), float64: Sinkhorn to 1e-13 "
-                      "with a Newton cross-check, then the eq (13) backward; %.1f s wall"
-                      % (Bs, "all of it" if Bs == w.B else "a prefix", dt)}
+                      "(cap %d sweeps) with a Newton cross-check%s; %.1f s wall"
+                      % (Bs, "all of it" if Bs == w.B else "a prefix", w.sk_cap,
+                         "" if fwd_only else ", then the eq (13) backward", dt)}
 
 
 def eot_cpu_baseline(w, target_s: float = 10.0):
@@ -171,7 +205,6 @@ def eot_report(w, args, dev):
     kern = {"birkhoff_eot_fwd": (fwd_ms, b_fwd), "birkhoff_eot_bwd": (bwd_ms, b_bwd)}
     dom = max(kern, key=lambda k: kern[k][0])
     d_ms, d_bytes = kern[dom]
-    achieved = d_bytes / (d_ms * 1e-3) / 1e9
     digest = hipbuild.kernel_source_digest()
     return {
         "metric": "%dx%d entropic OT plans/sec (fwd+bwd, fp32, general cost / marginals / eta) on 1 MI355X; "
@@ -181,9 +214,7 @@ def eot_report(w, args, dev):
         "data": "synthetic",
         "config": {"workload": "%s: %s" % (w.key, w.title), "B": B, "n": n, "m": m, "eta": w.eta,
                    "shared_marginals": w.shared, "passes": "fwd+bwd", "tol": w.tol, "max_iter": w.max_iter},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.key, dom, digest),
-                     "algorithmic_bytes_per_launch": d_bytes, "avg_launch_ms": d_ms},
+        "roofline": roofline(w.key, dom, d_bytes, d_ms, digest),
         "kernels_ms": {"birkhoff_eot_fwd": fwd_ms, "birkhoff_eot_bwd": bwd_ms},
         "kernels_hbm_frac": {k: v[1] / (v[0] * 1e-3) / 1e9 / HBM_PEAK_GBS for k, v in kern.items()},
         "newton": {"iterations_mean": float(it[it >= 0].mean()), "wave_max_mean": float(waves.max(1).mean()),
@@ -288,7 +319,6 @@ def mix_report(w, args, dev):
     kern = {"birkhoff_fwd_mix": (fwd_ms, b_fwd), "birkhoff_mix_bwd": (bwd_ms, b_bwd)}
     dom = max(kern, key=lambda k: kern[k][0])
     d_ms, d_bytes = kern[dom]
-    achieved = d_bytes / (d_ms * 1e-3) / 1e9
     digest = hipbuild.kernel_source_digest()
     return {
         "metric": "mHC tokens/sec: 4x4 projection + residual mixing y = T x and its backward (C=%d, %s streams) "
@@ -298,9 +328,7 @@ def mix_report(w, args, dev):
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": "%s: %s" % (w.key, w.title), "B": B, "C": C, "storage": w.io,
                    "passes": "fwd+bwd", "tol": w.tol, "max_iter": w.max_iter},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.key, dom, digest),
-                     "algorithmic_bytes_per_launch": d_bytes, "avg_launch_ms": d_ms},
+        "roofline": roofline(w.key, dom, d_bytes, d_ms, digest),
         "kernels_ms": {"birkhoff_fwd_mix": fwd_ms, "birkhoff_mix_bwd": bwd_ms},
         "kernels_hbm_frac": {k: v[1] / (v[0] * 1e-3) / 1e9 / HBM_PEAK_GBS for k, v in kern.items()},
         "torch_matmul_y_ms": torch_ms,
@@ -378,9 +406,7 @@ def forward_only_report(w, args, dev):
         "data": "synthetic",
         "config": {"workload": "%s: %s" % (w.key, w.title), "B": B, "n": n, "storage": w.io, "passes": "fwd",
                    "tol": w.tol, "max_iter": w.max_iter},
-        "roofline": {"bound": "alu", "kernel": "birkhoff_fwd", "hbm_achieved_GBs": b / (ms * 1e-3) / 1e9,
-                     "hbm_frac": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": measured_traffic(w.key, "birkhoff_fwd", digest),
-                     "algorithmic_bytes_per_launch": b, "avg_launch_ms": ms},
+        "roofline": roofline(w.key, "birkhoff_fwd", b, ms, digest),
         "newton": dict(score(st["T"]), iterations_hist=hist, iterations_mean=float(it[it >= 0].mean()),
                        wave_max_mean=float(waves.max(1).mean()), unconverged=int((it < 0).sum())),
         "sinkhorn20": dict(score(st["S"]), ms_per_launch=ms_sk, value=B / (ms_sk * 1e-3)),
@@ -531,9 +557,7 @@ def forward_backward_report(w, args, dev):
     dom = max(kern, key=lambda k: kern[k][0])
     d_ms, d_bytes = kern[dom]
     step_bytes = b_fused if args.path == "fused" else b_fwd + b_bwd
-    achieved = d_bytes / (d_ms * 1e-3) / 1e9
     digest = hipbuild.kernel_source_digest()
-    traffic = measured_traffic(w.key, dom, digest)
 
     out = {
         "metric": METRIC if (n == 4 and w.io == "f32") else
@@ -552,9 +576,7 @@ def forward_backward_report(w, args, dev):
         "data": "synthetic",
         "config": {"workload": "%s: %s" % (w.key, w.title), "B": B, "n": n, "storage": w.io,
                    "passes": "fwd+bwd", "path": args.path, "tol": w.tol, "max_iter": w.max_iter},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "algorithmic_bytes_per_launch": d_bytes, "avg_launch_ms": d_ms},
+        "roofline": roofline(w.key, dom, d_bytes, d_ms, digest),
         "kernels_ms": {"birkhoff_fwd_bwd": fused_ms, "birkhoff_fwd": fwd_ms, "birkhoff_bwd": bwd_ms},
         "step_hbm": {"algorithmic_bytes": step_bytes,
                      "achieved_GBs": step_bytes / (ms_step * 1e-3) / 1e9,

@@ -637,7 +637,7 @@ __device__ __forceinline__ void store_forward(const Geometry<N, IO>& geo, uint4*
 }
 
 template <int N, typename IO, bool kStats>
-__global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(N == 4 ? 7 : 4)))
+__global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(N == 4 ? 7 : 3)))
 newton_fwd_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, float* __restrict__ dual,
                   int32_t* __restrict__ iters, int64_t B, float tol, int max_iter) {
     using G = Geometry<N, IO>;
@@ -781,7 +781,7 @@ implicit_bwd_from_T_kernel(const float* __restrict__ Tin, const float* __restric
 // read back.  Reads logits and dT, writes T, dual and dH.
 // ---------------------------------------------------------------------------
 template <int N, typename IO>
-__global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(N == 4 ? 6 : 4)))
+__global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(N == 4 ? 6 : 3)))
 fused_fwd_bwd_kernel(const IO* __restrict__ logits, const IO* __restrict__ dT, IO* __restrict__ Tout,
                      float* __restrict__ dual, IO* __restrict__ dH, int64_t B, float tol, int max_iter) {
     using Gm = Geometry<N, IO>;

@@ -45,6 +45,11 @@ def entry_of(kernel_name: str):
     return None
 
 
+def stats_variant(kernel_name: str) -> bool:
+    """The forward kernels' variant that also writes iteration counts (template flag true)."""
+    return "fwd_kernel<" in kernel_name and "true>" in kernel_name
+
+
 def one_csv(d: pathlib.Path, suffix: str) -> pathlib.Path:
     found = sorted(pathlib.Path(d).rglob("*" + suffix))
     if not found:
@@ -87,6 +92,19 @@ def counters(d):
     for r in csv.DictReader(open(one_csv(d, "_counter_collection.csv"))):
         out[(r["Kernel_Name"], r["Counter_Name"])].append(float(r["Counter_Value"]))
     return out
+
+
+def last_copy(d, counter):
+    """The counter's reading for the run's last device copy: bench.py's
+    calibration copies come after all timed work, so the last copy dispatch is
+    one of them (uploads of inputs earlier in the run may have any size)."""
+    best = None
+    for r in csv.DictReader(open(one_csv(d, "_counter_collection.csv"))):
+        if COPY_KERNEL in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            k = int(r["Dispatch_Id"])
+            if best is None or k > best[0]:
+                best = (k, float(r["Counter_Value"]))
+    return None if best is None else best[1]
 
 
 def per_kernel(cnt, counter):
@@ -140,18 +158,23 @@ def main():
             lines.append("| `%s` | %s | %d | %.2f |" % (k.split("(")[0], entry_of(k) or "-", cnt, avg))
         if k_run < len(a.bench_json):
             b = json.loads(pathlib.Path(a.bench_json[k_run]).read_text().strip().splitlines()[-1])
+            per = b.get("kernels_ms")
+            if per is None:   # forward-only report: the forward and the Sinkhorn baseline
+                per = {"birkhoff_fwd": b["ms_per_step"]}
+                if "sinkhorn20" in b:
+                    per["sinkhorn_fwd"] = b["sinkhorn20"]["ms_per_launch"]
             lines += ["", "bench.py's own HIP-event figures in the same run (path `%s`): %s ms per step; "
                       "per-kernel average launch %s ms." % (
                           b["config"].get("path", "separate"), round(b["ms_per_step"], 5),
-                          {k: round(v, 5) for k, v in b["kernels_ms"].items()})]
+                          {k: round(v, 5) for k, v in per.items()})]
     (out / ("kernels_%s.md" % a.workload)).write_text("\n".join(lines) + "\n")
 
     fc, wc = counters(a.fetch), counters(a.write)
     f_k, w_k = per_kernel(fc, "FETCH_SIZE"), per_kernel(wc, "WRITE_SIZE")
     copy_bytes = a.copy_mib << 20
-    f_copy = [v for k, v in f_k.items() if COPY_KERNEL in k]
-    w_copy = [v for k, v in w_k.items() if COPY_KERNEL in k]
-    if not f_copy or not w_copy:
+    f_copy = [last_copy(a.fetch, "FETCH_SIZE")]
+    w_copy = [last_copy(a.write, "WRITE_SIZE")]
+    if f_copy[0] is None or w_copy[0] is None:
         raise SystemExit("the counter runs hold no %s dispatch to calibrate against" % COPY_KERNEL)
     f_scale = copy_bytes / f_copy[0]     # bytes per FETCH_SIZE unit
     w_scale = copy_bytes / w_copy[0]     # bytes per WRITE_SIZE unit
@@ -163,7 +186,8 @@ def main():
             continue
         rd = f_k.get(k, float("nan")) * f_scale
         wr = w_k.get(k, float("nan")) * w_scale
-        traffic[e] = rd + wr
+        if not stats_variant(k):   # the timed launches are the ones without iteration counts
+            traffic[e] = rd + wr
         rows.append("| `%s` | %s | %.0f | %.0f | %.1f | %.1f | %.1f |" % (
             k.split("(")[0], e, f_k.get(k, float("nan")), w_k.get(k, float("nan")), rd / 1e6, wr / 1e6,
             (rd + wr) / 1e6))
@@ -171,7 +195,8 @@ def main():
            "Commands (run from /tmp with TMPDIR=/tmp; `$R` is the repository root):", "",
            "    " + a.cmd_fetch, "    " + a.cmd_write, "",
            "FETCH_SIZE and WRITE_SIZE are in KiB per dispatch as rocprofv3 reports them. The same runs copy "
-           "%d MiB once per call with a device copy kernel (`%s`); its readings (FETCH %.0f, WRITE %.0f) give "
+           "%d MiB five times at their end with a device copy kernel (`%s`); the last copy's readings "
+           "(FETCH %.0f, WRITE %.0f) give "
            "the factors that turn the counters into bytes: %.4f bytes per FETCH unit and %.4f per WRITE unit "
            "(a counter that counted KiB exactly would give 1024)." % (
                a.copy_mib, COPY_KERNEL, f_copy[0], w_copy[0], f_scale, w_scale), "",
@@ -189,10 +214,16 @@ def main():
         for k in kern:
             doc.append("| `%s` | " % k.split("(")[0] + " | ".join(
                 "%.4g" % statistics.median(sq[(k, c)]) if (k, c) in sq else "-" for c in names) + " |")
+    valu = {}
+    if a.sq:
+        for (k, c), v in counters(a.sq).items():
+            e = entry_of(k)
+            if e is not None and c == "SQ_INSTS_VALU" and not stats_variant(k):
+                valu[e] = statistics.median(v)
     (out / ("traffic_%s.md" % a.workload)).write_text("\n".join(doc) + "\n")
     (out / ("traffic_%s.json" % a.workload)).write_text(json.dumps(
         {"workload": a.workload, "kernel_digest": digest, "bytes_per_launch": traffic,
-         "fetch_scale": f_scale, "write_scale": w_scale}, indent=1) + "\n")
+         "valu_insts_per_launch": valu, "fetch_scale": f_scale, "write_scale": w_scale}, indent=1) + "\n")
     print("\n".join(lines + [""] + doc))
 
 

@@ -1,7 +1,8 @@
 """Code-generation checks on the gfx950 assembly of the kernels (CPU only: hipcc
 cross-compiles).  They pin properties the measured performance depends on:
 every matrix / dual store is non-temporal, the n = 4 kernels keep their
-occupancy and spill nothing, the n = 8 loops keep four waves per SIMD, and the
+occupancy and spill nothing, the n = 8 kernels keep three waves per SIMD without
+spilling, and the
 general-OT kernels spill nothing and stream their stores too."""
 import re
 import shutil
@@ -65,12 +66,20 @@ def test_n4_kernels_occupancy_and_no_spills(asm):
             assert scratch == 0 and o >= occ, (key, vgpr, scratch, o)
 
 
-def test_n8_forward_keeps_four_waves(asm):
+def test_n8_kernels_keep_three_waves_without_spills(asm):
+    """At four waves per SIMD (128 VGPRs) the n = 8 fused kernel spilled 104 bytes
+    per lane, which showed up as 0.5 GB of extra HBM traffic per launch; three
+    waves and no scratch measured 18 % faster."""
     ks = kernels(asm)
-    hits = [v for k, v in ks.items() if "newton_fwd_kernelILi8Ef" in k or "fused_fwd_bwd_kernelILi8Ef" in k]
+    hits = [v for k, v in ks.items() if "ILi8E" in k and "sinkhorn" not in k]
     assert hits
     for _, vgpr, scratch, o in hits:
-        assert o >= 4, (vgpr, scratch, o)
+        assert o >= 3 and scratch == 0, (vgpr, scratch, o)
+
+
+def test_no_kernel_uses_scratch(asm):
+    for name, (_, vgpr, scratch, _o) in kernels(asm).items():
+        assert scratch == 0, (name, vgpr, scratch)
 
 
 def test_eot_kernels_stream_and_do_not_spill(asm_eot):
