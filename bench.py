@@ -17,10 +17,8 @@ cache.  The timed region is `--steps` back-to-back steps between two HIP events
 on the stream the kernels run on; `value` is B / (time per step).
 
 The roofline figure is for the kernel with the longer average launch time
-(the fused kernel is the only one of its step).  It is an HBM figure unless the
-committed counters for the same kernel sources show the vector ALUs busier
-than HBM; then the kernel is reported as ALU-bound, against the VALU issue peak
-(see roofline()).  Each separate kernel's
+(the fused kernel is the only one of its step); see roofline() for the VALU
+figure that accompanies it when counters for the same kernel sources exist.  Each separate kernel's
 average launch time is measured as `--steps` back-to-back launches of that
 kernel alone (alternating the two sets) between two HIP events on the same
 stream -- events between the two kernels of a step would themselves add gaps.
@@ -50,7 +48,8 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak, GB/s
 METRIC = "4x4 Birkhoff projections/sec (fwd+bwd, fp32) on 1 MI355X; % HBM roofline"
 
 
-VALU_PEAK = 256 * 4 * 16 * 2.4e9   # lane-instructions/s: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+CLOCK_HZ = 2.4e9   # MI355X peak engine clock
+N_CU = 256
 
 
 def _profile(workload: str, digest: str):
@@ -68,24 +67,18 @@ def measured_traffic(workload: str, kernel: str, digest: str):
 
 
 def roofline(workload: str, kernel: str, nbytes: float, ms: float, digest: str) -> dict:
-    """The dominant kernel against its bound.  HBM: algorithmic bytes per launch
-    over the launch time, against 8 TB/s.  When the committed counters (same
-    kernel sources) show the vector ALUs busier than HBM, the kernel is reported
-    as ALU-bound: VALU lane-instructions per launch (SQ_INSTS_VALU x 64) over the
-    launch time, against the issue peak of 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
-    = 39.3e12 lane-instructions/s; the HBM figures stay alongside."""
+    """The dominant kernel against the HBM roofline: algorithmic bytes per launch
+    over the launch time, against 8 TB/s.  When committed counters exist for the
+    same kernel sources, `valu_busy` adds AMD's VALUBusy measure for the same
+    launch time -- SQ_ACTIVE_INST_VALU / (CUs x cycles), cycles = time x 2.4 GHz --
+    which an issue-saturated fp32 FMA loop drives to about 0.9 on this chip."""
     hbm = nbytes / (ms * 1e-3) / 1e9
     out = {"bound": "hbm", "kernel": kernel, "achieved": hbm, "peak": HBM_PEAK_GBS, "unit": "GB/s",
            "frac": hbm / HBM_PEAK_GBS, "traffic": measured_traffic(workload, kernel, digest),
            "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": ms}
-    valu = _profile(workload, digest).get("valu_insts_per_launch", {}).get(kernel)
-    if valu is not None:
-        rate = valu * 64 / (ms * 1e-3)
-        out["valu_frac"] = rate / VALU_PEAK
-        if rate / VALU_PEAK > hbm / HBM_PEAK_GBS:
-            out.update({"bound": "alu", "achieved": rate / 1e12, "peak": VALU_PEAK / 1e12,
-                        "unit": "T lane-instr/s", "frac": rate / VALU_PEAK, "hbm_GBs": hbm,
-                        "hbm_frac": hbm / HBM_PEAK_GBS})
+    active = _profile(workload, digest).get("valu_active_per_launch", {}).get(kernel)
+    if active is not None:
+        out["valu_busy"] = active / N_CU / (ms * 1e-3 * CLOCK_HZ)
     return out
 
 

@@ -214,16 +214,21 @@ def main():
         for k in kern:
             doc.append("| `%s` | " % k.split("(")[0] + " | ".join(
                 "%.4g" % statistics.median(sq[(k, c)]) if (k, c) in sq else "-" for c in names) + " |")
-    valu = {}
+    valu, active = {}, {}
     if a.sq:
         for (k, c), v in counters(a.sq).items():
             e = entry_of(k)
-            if e is not None and c == "SQ_INSTS_VALU" and not stats_variant(k):
+            if e is None or stats_variant(k):
+                continue
+            if c == "SQ_INSTS_VALU":
                 valu[e] = statistics.median(v)
+            elif c == "SQ_ACTIVE_INST_VALU":
+                active[e] = statistics.median(v)
     (out / ("traffic_%s.md" % a.workload)).write_text("\n".join(doc) + "\n")
     (out / ("traffic_%s.json" % a.workload)).write_text(json.dumps(
         {"workload": a.workload, "kernel_digest": digest, "bytes_per_launch": traffic,
-         "valu_insts_per_launch": valu, "fetch_scale": f_scale, "write_scale": w_scale}, indent=1) + "\n")
+         "valu_insts_per_launch": valu, "valu_active_per_launch": active,
+         "fetch_scale": f_scale, "write_scale": w_scale}, indent=1) + "\n")
     print("\n".join(lines + [""] + doc))
 
 
