@@ -365,7 +365,7 @@ struct Lanes {
     __device__ __forceinline__ int64_t problem() const { return base + lane; }
 };
 
-// Forward: Newton on the reduced dual (eq 8) from one Sinkhorn sweep until the column
+// Forward: Newton on the reduced dual (eq 8) from kStartSweeps Sinkhorn sweeps until the column
 // marginals are met to `tol` (absolute) or `max_iter` updates; rows are met by
 // construction.  Step sizes 1, 1/2, 1/10, 1/20, 1/100, the first that lowers
 // both the objective and the gradient norm is taken; otherwise one Sinkhorn
@@ -389,12 +389,13 @@ eot_fwd_kernel(const float* __restrict__ cost, const float* __restrict__ a_in, c
     float a[N], b[M];
     load_marginal<N>(a_in, shared, ln.base, ln.nvalid, lds, ln.lane, a);
     load_marginal<M>(b_in, shared, ln.base, ln.nvalid, lds, ln.lane, b);
-    // start: one Sinkhorn-Knopp sweep (eqs 5-6) from z = log(b / b_{m-1}) (base 2
-    // here), i.e. the rows normalised at that z and then the columns scaled to b:
-    // z_j += log(b_j / c_j) - log(b_{m-1} / c_{m-1}).  It is the optimum when the
-    // cost is constant (plan a b^T / sum(b)) and the Birkhoff kernels' start when
-    // a = b = 1.  The sweep is skipped if a column sum is 0 or not finite; lanes
-    // past the end (b = 0) start at 0.
+    // start: kStartSweeps Sinkhorn-Knopp sweeps (eqs 5-6) from z = log(b / b_{m-1})
+    // (base 2 here): the rows normalised at that z, then per sweep the columns
+    // scaled to b and the rows normalised again, z_j += log(b_j / c_j) -
+    // log(b_{m-1} / c_{m-1}).  It is the optimum when the cost is constant (plan
+    // a b^T / sum(b)) and the Birkhoff kernels' start when a = b = 1.  A sweep is
+    // skipped if a column sum is 0 or not finite; lanes past the end (b = 0)
+    // start at 0.
     float S[N * M], y[K1], c[M];
     {
         const float lbm = ln.valid() ? lg2(b[K1]) : 0.0f;
@@ -406,9 +407,10 @@ eot_fwd_kernel(const float* __restrict__ cost, const float* __restrict__ a_in, c
         for (int k = 0; k < N * M; ++k) L[k] *= lscale;
         softmax_rows<M, N>(L, y, S);
     }
-    col_sums<N, M>(S, a, c);
-    {
-        // the sweep's column step: S_ij <- S_ij b_j / c_j, rows normalised again
+#pragma unroll
+    for (int sw = 0; sw < kStartSweeps; ++sw) {
+        // a sweep's column step: S_ij <- S_ij b_j / c_j, rows normalised again
+        col_sums<N, M>(S, a, c);
         bool ok = ln.valid();
 #pragma unroll
         for (int j = 0; j < M; ++j) ok = ok && c[j] > 1.17549435e-38f && c[j] < 3.0e38f;

@@ -33,6 +33,8 @@
 namespace birk {
 
 constexpr int kBlock = 256;  // threads per workgroup (4 waves of 64)
+// Sinkhorn-Knopp sweeps that give Newton's starting point (not counted as updates)
+constexpr int kStartSweeps = 3;
 
 // lanes per matrix
 template <int N>
@@ -495,8 +497,8 @@ __device__ __forceinline__ void load_own(const IO* __restrict__ p, int64_t item,
 // Forward: Newton on the reduced dual (eq 8).
 // ---------------------------------------------------------------------------
 
-// Loads the wave's logits, evaluates T at the start x^(0) (one Sinkhorn sweep
-// from beta = 0) and runs Newton's method to
+// Loads the wave's logits, evaluates T at the start x^(0) (kStartSweeps
+// Sinkhorn sweeps from beta = 0) and runs Newton's method to
 // column-sum residual <= tol or max_iter updates.  On return T is the lane's
 // rows of the last iterate, y the dual (base-2 units, y_{N-1} = 0 implied),
 // res its residual; returns the number of updates.  The logits are needed
@@ -523,13 +525,16 @@ __device__ __forceinline__ int newton_solve(const Geometry<N, IO>& geo, uint4* l
     // optionally start copying another tile of the wave (dL/dT) into the now
     // free LDS region, to be read after the iteration
     if constexpr (kPrefetch) G::Tile::prefetch(geo.chunks(prefetch_src), geo.nvalid * G::C, lds, geo.lane);
-    // start: the dual after one Sinkhorn-Knopp sweep from v = 1 -- the rows of
-    // exp(H) normalised (T at beta = 0 above), then its columns scaled to sum to
-    // one and the rows normalised again, which is T at
-    // beta_j = log c_{n-1} - log c_j; kept at beta = 0 if a column sum is 0 or
-    // not finite
-    col_sums<N>(T, c);
-    {
+    // start: the dual after kStartSweeps Sinkhorn-Knopp sweeps from v = 1.  The
+    // rows of exp(H) are normalised above (T at beta = 0); each sweep scales the
+    // columns of T to sum to one and normalises the rows again, which moves the
+    // dual by beta_j += log c_{n-1} - log c_j.  A sweep whose column sums are 0 or
+    // not finite is skipped.
+#pragma unroll
+    for (int j = 0; j < M; ++j) y[j] = 0.0f;
+#pragma unroll
+    for (int sw = 0; sw < kStartSweeps; ++sw) {
+        col_sums<N>(T, c);
         bool ok = true;
 #pragma unroll
         for (int j = 0; j < N; ++j) ok = ok && c[j] > 1.17549435e-38f && c[j] < 3.0e38f;
@@ -537,7 +542,7 @@ __device__ __forceinline__ int newton_solve(const Geometry<N, IO>& geo, uint4* l
 #pragma unroll
         for (int j = 0; j < N; ++j) rc[j] = ok ? rcp(c[j]) : 1.0f;
 #pragma unroll
-        for (int j = 0; j < M; ++j) y[j] = ok ? lg2(c[N - 1] * rc[j]) : 0.0f;
+        for (int j = 0; j < M; ++j) y[j] += ok ? lg2(c[N - 1] * rc[j]) : 0.0f;
 #pragma unroll
         for (int i = 0; i < K; ++i) {
             float rs = 0.0f;

@@ -58,6 +58,8 @@
 #endif
 
 #define ORACLE_NMAX 16
+/* Sinkhorn-Knopp sweeps that give Newton's starting point (not updates) */
+#define START_SWEEPS 3
 
 /* ------------------------------------------------------------------ */
 /* small helpers                                                        */
@@ -252,11 +254,13 @@ static double colsum_residual(const double *c, int n)
     return r;
 }
 
-/* Newton's method for min_x f(x), x = beta_{-n} (eq 8), from the dual after one
- * Sinkhorn-Knopp sweep from beta = 0 (the pages leave x^(0) open): the rows of
- * exp(H) normalised (T at beta = 0), then its columns scaled to sum to one,
- *   beta_j = -log c_j + log c_n,  c = column sums of T at beta = 0,
- * which is not counted as an update (kept at 0 when a column sum underflows).
+/* Newton's method for min_x f(x), x = beta_{-n} (eq 8), from the dual after
+ * START_SWEEPS Sinkhorn-Knopp sweeps from beta = 0 (the pages leave x^(0) open):
+ * each sweep scales the columns of the row-normalised T to sum to one,
+ *   beta_j <- beta_j - log c_j + log c_n,  c = column sums of T at beta,
+ * and the rows are normalised again (T = rows of softmax(H + beta)).  The
+ * sweeps are not counted as updates; they stop early if a column sum
+ * underflows.
  *   gradient  g = c_{-n} - 1                           (eq 9, a = b = 1)
  *   Hessian   diag(c_{-n}) - T_{-n}^T T_{-n}           (eq 9, eta = 1)
  *   step      x+ = x + gamma d,  d = -Hess^{-1} g
@@ -284,9 +288,11 @@ static int newton_one(const double *H, int n, double tol, int max_iter,
     eval_T(H, n, beta, T, c);
     int ok = 1;
     for (int j = 0; j < n; ++j) ok = ok && c[j] > 0.0 && isfinite(c[j]);
-    if (ok) {
-        for (int j = 0; j < n; ++j) beta[j] = -log(c[j]) + log(c[n - 1]);
+    for (int sw = 0; sw < START_SWEEPS && ok; ++sw) {
+        const double lcn = log(c[n - 1]);
+        for (int j = 0; j < n; ++j) beta[j] += -log(c[j]) + lcn;
         eval_T(H, n, beta, T, c);
+        for (int j = 0; j < n; ++j) ok = ok && c[j] > 0.0 && isfinite(c[j]);
     }
     int it = 0, conv = 0;
     for (;;) {
@@ -497,13 +503,13 @@ static void eot_eval_T(const double *M, const double *a, int n, int m, double et
     }
 }
 
-/* Newton's method on the reduced dual (eq 8), from the dual after one
- * Sinkhorn-Knopp sweep (eqs 5-7) from beta = eta log(b / b_m) (the pages leave
+/* Newton's method on the reduced dual (eq 8), from the dual after START_SWEEPS
+ * Sinkhorn-Knopp sweeps (eqs 5-7) from beta = eta log(b / b_m) (the pages leave
  * x^(0) open; this reduces to newton_one's start when a = b = 1 and eta = 1, and
  * is already the optimum when the cost is constant, whose plan is
- * a b^T / sum(b)): with c the column sums of T at that beta,
+ * a b^T / sum(b)): each sweep, with c the column sums of T at beta,
  *   beta_j <- beta_j + eta (log(b_j / c_j) - log(b_m / c_m)),
- * not counted as an update (skipped when a column sum underflows):
+ * not counted as updates (they stop when a column sum underflows):
  *   gradient  g = c_{-m} - b_{-m}                                   (eq 9)
  *   Hessian   eta^-1 [diag(c_{-m}) - T_{-m}^T diag(a)^-1 T_{-m}]    (eq 9)
  * with the step-size rule and Sinkhorn fallback of [B] section 2.2, as in
@@ -525,10 +531,11 @@ static int eot_newton_one(const double *M, const double *a, const double *b, int
     eot_eval_T(M, a, n, m, eta, beta, T, c);
     int ok = 1;
     for (int j = 0; j < m; ++j) ok = ok && c[j] > 0.0 && isfinite(c[j]);
-    if (ok) {
+    for (int sw = 0; sw < START_SWEEPS && ok; ++sw) {
         const double cm = log(b[m - 1] / c[m - 1]);
         for (int j = 0; j < m; ++j) beta[j] += eta * (log(b[j] / c[j]) - cm);
         eot_eval_T(M, a, n, m, eta, beta, T, c);
+        for (int j = 0; j < m; ++j) ok = ok && c[j] > 0.0 && isfinite(c[j]);
     }
     int it = 0, conv = 0;
     for (;;) {

@@ -234,8 +234,8 @@ def test_reduced_dual_with_library_minimiser(n):
 @pytest.mark.parametrize("n", [3, 4, 8])
 def test_first_newton_step_from_the_sweep_start(n):
     """One Newton update (the full step, on mild inputs) from the start x0 = the dual
-    after one Sinkhorn sweep from v = 1, i.e. beta_j = -log c_j + log c_n with c the
-    column sums of the row-normalised exp(H): x1 = x0 - H^{-1} g with g and H the
+    after three Sinkhorn sweeps from v = 1, each beta_j += -log c_j + log c_n with c the
+    column sums of the row-normalised exp(H + beta): x1 = x0 - H^{-1} g with g and H the
     finite-difference gradient and Hessian of eq (8) at x0."""
     rng = np.random.default_rng(50 + n)
     H = 0.3 * rng.standard_normal((5, n, n))
@@ -247,8 +247,11 @@ def test_first_newton_step_from_the_sweep_start(n):
             beta = np.append(x, 0.0)
             return n + logsumexp(Hq + beta[None, :], axis=1).sum() - beta.sum()
 
-        c = softmax(Hq, axis=1).sum(axis=0)
-        x0 = -np.log(c[:-1]) + np.log(c[-1])
+        beta = np.zeros(n)
+        for _ in range(3):
+            c = softmax(Hq + beta[None, :], axis=1).sum(axis=0)
+            beta = beta - np.log(c) + np.log(c[-1])
+        x0 = beta[:-1]
         k, h = n - 1, 1e-4
         E = np.eye(k) * h
         g = np.array([(f(x0 + E[i]) - f(x0 - E[i])) / (2 * h) for i in range(k)])

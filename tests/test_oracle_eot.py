@@ -208,7 +208,7 @@ def test_reduced_dual_with_library_minimiser(n, m):
 def test_first_newton_step_matches_finite_difference_newton(eta):
     """One Newton update from the start on a mild problem (the full step is taken):
     x1 = x0 - H^{-1} g, with g and H the finite-difference gradient and Hessian of eq (8)
-    at x0, the dual after one Sinkhorn sweep (eqs 5-6) from beta = eta log(b / b_m)."""
+    at x0, the dual after three Sinkhorn sweeps (eqs 5-6) from beta = eta log(b / b_m)."""
     rng = np.random.default_rng(108)
     n, m = 4, 5
     M, a, b = problem(rng, 6, n, m, sigma=0.3 * eta)
@@ -222,9 +222,10 @@ def test_first_newton_step_matches_finite_difference_newton(eta):
             return eta * aq.sum() - alpha @ aq - beta @ bq
 
         k, h = m - 1, 1e-4 * eta
-        b_start = eta * (np.log(bq) - np.log(bq[-1]))
-        a_sweep = eta * np.log(aq) - eta * logsumexp((b_start[None, :] - Mq) / eta, axis=1)   # eq (5)
-        b_sweep = eta * np.log(bq) - eta * logsumexp((a_sweep[:, None] - Mq) / eta, axis=0)  # eq (6)
+        b_sweep = eta * (np.log(bq) - np.log(bq[-1]))
+        for _ in range(3):
+            a_sweep = eta * np.log(aq) - eta * logsumexp((b_sweep[None, :] - Mq) / eta, axis=1)   # eq (5)
+            b_sweep = eta * np.log(bq) - eta * logsumexp((a_sweep[:, None] - Mq) / eta, axis=0)  # eq (6)
         x0 = b_sweep[:-1] - b_sweep[-1]
         E = np.eye(k) * h
         g = np.array([(f(x0 + E[i]) - f(x0 - E[i])) / (2 * h) for i in range(k)])
@@ -235,7 +236,7 @@ def test_first_newton_step_matches_finite_difference_newton(eta):
 
 
 def test_constant_cost_needs_no_update():
-    """A constant cost has the plan a b^T / sum(b); the start (one sweep from
+    """A constant cost has the plan a b^T / sum(b); the start (sweeps from
     eta log(b / b_m)) is already optimal, so Newton stops before its first update."""
     rng = np.random.default_rng(115)
     M, a, b = problem(rng, 8, 3, 6)
