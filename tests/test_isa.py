@@ -32,6 +32,11 @@ def asm(tmp_path_factory):
 
 
 @pytest.fixture(scope="module")
+def asm_mix(tmp_path_factory):
+    return compile_asm(tmp_path_factory, "mix.hip")
+
+
+@pytest.fixture(scope="module")
 def asm_eot(tmp_path_factory):
     """The general-OT kernels for n = 4 and 5 rows (every column count)."""
     return compile_asm(tmp_path_factory, "eot_rows_45.hip")
@@ -91,3 +96,23 @@ def test_eot_kernels_stream_and_do_not_spill(asm_eot):
             assert line.rstrip().endswith(" nt"), (name, line)
     small = [v for k, v in ks.items() if "eot_fwd_kernelILi4ELi4E" in k]
     assert small and all(o >= 4 for _, _, _, o in small)
+
+
+SCALAR_WRITES = re.compile(r"^\s+s_(store|buffer_store|scratch_store|atomic|buffer_atomic|dcache_wb|dcache_discard)",
+                           re.M)
+
+
+def test_no_kernel_writes_through_the_scalar_cache(asm, asm_eot, asm_mix):
+    """Every store and atomic of the library is a vector-memory instruction: no
+    scalar-memory stores, atomics, write-backs or discards in any kernel."""
+    for text in (asm, asm_eot, asm_mix):
+        assert not SCALAR_WRITES.findall(text)
+
+
+def test_mix_kernels_stream_and_do_not_spill(asm_mix):
+    ks = kernels(asm_mix)
+    assert len(ks) == 4
+    for name, (body, vgpr, scratch, occ) in ks.items():
+        assert scratch == 0 and occ >= 3, (name, vgpr, occ)
+        for line in re.findall(r"^\s+global_store_dwordx4.*$", body, flags=re.M):
+            assert line.rstrip().endswith(" nt"), (name, line)
