@@ -55,12 +55,21 @@ dim3 grid_for(int64_t B, int n) {
 template <int N, typename IO>
 int fwd_launch(const IO* logits, IO* T, float* dual, int32_t* iters, int64_t B, float tol, int max_iter,
                hipStream_t s) {
-    if (iters)
-        hipLaunchKernelGGL((birk::newton_fwd_kernel<N, IO, true>), grid_for(B, N), dim3(kBlock), 0, s, logits, T,
-                           dual, iters, B, tol, max_iter);
-    else
-        hipLaunchKernelGGL((birk::newton_fwd_kernel<N, IO, false>), grid_for(B, N), dim3(kBlock), 0, s, logits, T,
-                           dual, iters, B, tol, max_iter);
+    if constexpr (N == 4) {
+        if (iters)
+            hipLaunchKernelGGL((birk::newton_fwd_gather_kernel<IO, true>), grid_for(B, N), dim3(kBlock), 0, s,
+                               logits, T, dual, iters, B, tol, max_iter);
+        else
+            hipLaunchKernelGGL((birk::newton_fwd_gather_kernel<IO, false>), grid_for(B, N), dim3(kBlock), 0, s,
+                               logits, T, dual, iters, B, tol, max_iter);
+    } else {
+        if (iters)
+            hipLaunchKernelGGL((birk::newton_fwd_kernel<N, IO, true>), grid_for(B, N), dim3(kBlock), 0, s, logits,
+                               T, dual, iters, B, tol, max_iter);
+        else
+            hipLaunchKernelGGL((birk::newton_fwd_kernel<N, IO, false>), grid_for(B, N), dim3(kBlock), 0, s, logits,
+                               T, dual, iters, B, tol, max_iter);
+    }
     return launched();
 }
 

@@ -243,6 +243,23 @@ struct WaveTile {
         wave_lds_sync();
     }
 
+    // As store, but the items whose bit is set in the wave-uniform mask `skip`
+    // (bit m = the wave's m-th item) are not written.
+    __device__ __forceinline__ static void store_except(const uint4 (&own)[C], uint4* lds, int lane,
+                                                        uint4* __restrict__ dst, int valid, uint64_t skip) {
+        static_assert(kStaged, "staged tiles only");
+#pragma unroll
+        for (int q = 0; q < C; ++q) lds[slot(lane, q)] = own[q];
+        wave_lds_sync();
+#pragma unroll
+        for (int k = 0; k < C; ++k) {
+            const int c = chunk(k, lane);
+            const uint4 v = lds[slot(c / C, c % C)];
+            if (c < valid && !((skip >> (c / C)) & 1u)) stream_store(dst + c, v);
+        }
+        wave_lds_sync();
+    }
+
     // Registers of the owning lane -> global.  `valid` (wave-uniform) chunks
     // exist; the rest are not written.  A full tile stores unconditionally.
     __device__ __forceinline__ static void store(const uint4 (&own)[C], uint4* lds, int lane, uint4* __restrict__ dst,

@@ -497,22 +497,81 @@ __device__ __forceinline__ void load_own(const IO* __restrict__ p, int64_t item,
 // Forward: Newton on the reduced dual (eq 8).
 // ---------------------------------------------------------------------------
 
-// Loads the wave's logits, evaluates T at the start x^(0) (kStartSweeps
-// Sinkhorn sweeps from beta = 0) and runs Newton's method to
-// column-sum residual <= tol or max_iter updates.  On return T is the lane's
-// rows of the last iterate, y the dual (base-2 units, y_{N-1} = 0 implied),
-// res its residual; returns the number of updates.  The logits are needed
-// again only by the rare fallback sweep, which re-reads this lane's rows; they
-// do not stay in registers through the loop.
+// Newton's method on the reduced dual (eq 8) from the lane's current iterate
+// (T, y, its column sums c and residual res, it updates so far) until the
+// column-sum residual is <= tol or it reaches max_iter.  `item` is the lane's
+// item index, whose logits the rare fallback sweep re-reads.
+template <int N, typename IO>
+__device__ __forceinline__ void newton_iterate(const IO* __restrict__ logits, int64_t item, float tol, int max_iter,
+                                               float (&T)[Split<N>::K * N], float (&y)[N - 1], float (&c)[N],
+                                               float& res, int& it) {
+    constexpr int M = N - 1, K = Split<N>::K;
+    while (res > tol && it < max_iter) {
+        float g[M], r[M], d[M];
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+            g[j] = c[j] - 1.0f;
+            r[j] = -g[j];
+        }
+        float gn2 = g[0] * g[0];
+#pragma unroll
+        for (int j = 1; j < M; ++j) gn2 = fmaf(g[j], g[j], gn2);
+        float h[Tri<N>::S];
+        hessian<N>(T, h);
+        damp<N>(h);
+        const bool ok = SpdSolve<N>::run(h, r, d);   // d = -H^{-1} g
+
+        bool accepted = false;
+        if (ok) {
+            for (int k = 0; k < 5; ++k) {
+                const float gam = step_size(k);
+                float s[M], e[M], rr[K], ct[N];
+#pragma unroll
+                for (int j = 0; j < M; ++j) s[j] = gam * d[j];
+                float noise;
+                const float df = trial_point<N>(T, s, e, rr, ct, noise);
+                float gt2 = (ct[0] - 1.0f) * (ct[0] - 1.0f);
+#pragma unroll
+                for (int j = 1; j < M; ++j) gt2 = fmaf(ct[j] - 1.0f, ct[j] - 1.0f, gt2);
+                // the objective must not increase beyond what fp32 can resolve, and
+                // the gradient norm must decrease
+                if (df < noise && gt2 < gn2) {
+#pragma unroll
+                    for (int j = 0; j < M; ++j) y[j] = fmaf(s[j], kLog2e, y[j]);
+                    accept_trial<N>(T, e, rr);
+#pragma unroll
+                    for (int j = 0; j < N; ++j) c[j] = ct[j];
+                    accepted = true;
+                    break;
+                }
+            }
+        }
+        if (!accepted) {
+            float L[K * N];
+            load_own<N, IO>(logits, item, L);
+#pragma unroll
+            for (int k = 0; k < K * N; ++k) L[k] *= kLog2e;
+            sinkhorn_sweep<N>(L, y);
+            softmax_rows<N, K>(L, y, T);
+            col_sums<N>(T, c);
+        }
+        ++it;
+        res = col_residual<N>(c);
+    }
+}
+
+// Loads the wave's logits and evaluates the start x^(0) (kStartSweeps
+// Sinkhorn sweeps from beta = 0): T (the lane's rows), y (base-2 dual,
+// y_{N-1} = 0 implied), c (column sums of T) and res (their residual; 0 for
+// lanes past the end of the batch, which are thereby done).  The logits are
+// needed again only by the rare fallback sweep, which re-reads this lane's
+// rows; they do not stay in registers through the iteration.
 template <int N, typename IO, bool kPrefetch = false>
-__device__ __forceinline__ int newton_solve(const Geometry<N, IO>& geo, uint4* lds, const IO* __restrict__ logits,
-                                            float tol, int max_iter, float (&T_out)[Split<N>::K * N],
-                                            float (&y_out)[N - 1], float& res_out,
-                                            const IO* __restrict__ prefetch_src = nullptr) {
+__device__ __forceinline__ void newton_start(const Geometry<N, IO>& geo, uint4* lds, const IO* __restrict__ logits,
+                                             float (&T)[Split<N>::K * N], float (&y)[N - 1], float (&c)[N],
+                                             float& res, const IO* __restrict__ prefetch_src = nullptr) {
     constexpr int M = N - 1, K = Split<N>::K;
     using G = Geometry<N, IO>;
-    // the iteration works on locals, copied out at the end (keeps the loop in registers)
-    float T[K * N], y[M], c[N], res;
     {
         float L[K * N];
         uint4 w[G::C];
@@ -558,60 +617,23 @@ __device__ __forceinline__ int newton_solve(const Geometry<N, IO>& geo, uint4* l
     }
     col_sums<N>(T, c);
     res = geo.valid() ? col_residual<N>(c) : 0.0f;   // lanes past the end are done
+}
+
+// newton_start, then Newton's method to column-sum residual <= tol or max_iter
+// updates.  On return T is the lane's rows of the last iterate, y the dual
+// (base-2 units, y_{N-1} = 0 implied), res its residual; returns the number of
+// updates.
+template <int N, typename IO, bool kPrefetch = false>
+__device__ __forceinline__ int newton_solve(const Geometry<N, IO>& geo, uint4* lds, const IO* __restrict__ logits,
+                                            float tol, int max_iter, float (&T_out)[Split<N>::K * N],
+                                            float (&y_out)[N - 1], float& res_out,
+                                            const IO* __restrict__ prefetch_src = nullptr) {
+    constexpr int M = N - 1, K = Split<N>::K;
+    // the iteration works on locals, copied out at the end (keeps the loop in registers)
+    float T[K * N], y[M], c[N], res;
+    newton_start<N, IO, kPrefetch>(geo, lds, logits, T, y, c, res, prefetch_src);
     int it = 0;
-
-    while (res > tol && it < max_iter) {
-        float g[M], r[M], d[M];
-#pragma unroll
-        for (int j = 0; j < M; ++j) {
-            g[j] = c[j] - 1.0f;
-            r[j] = -g[j];
-        }
-        float gn2 = g[0] * g[0];
-#pragma unroll
-        for (int j = 1; j < M; ++j) gn2 = fmaf(g[j], g[j], gn2);
-        float h[Tri<N>::S];
-        hessian<N>(T, h);
-        damp<N>(h);
-        const bool ok = SpdSolve<N>::run(h, r, d);   // d = -H^{-1} g
-
-        bool accepted = false;
-        if (ok) {
-            for (int k = 0; k < 5; ++k) {
-                const float gam = step_size(k);
-                float s[M], e[M], rr[K], ct[N];
-#pragma unroll
-                for (int j = 0; j < M; ++j) s[j] = gam * d[j];
-                float noise;
-                const float df = trial_point<N>(T, s, e, rr, ct, noise);
-                float gt2 = (ct[0] - 1.0f) * (ct[0] - 1.0f);
-#pragma unroll
-                for (int j = 1; j < M; ++j) gt2 = fmaf(ct[j] - 1.0f, ct[j] - 1.0f, gt2);
-                // the objective must not increase beyond what fp32 can resolve, and
-                // the gradient norm must decrease
-                if (df < noise && gt2 < gn2) {
-#pragma unroll
-                    for (int j = 0; j < M; ++j) y[j] = fmaf(s[j], kLog2e, y[j]);
-                    accept_trial<N>(T, e, rr);
-#pragma unroll
-                    for (int j = 0; j < N; ++j) c[j] = ct[j];
-                    accepted = true;
-                    break;
-                }
-            }
-        }
-        if (!accepted) {
-            float L[K * N];
-            load_own<N, IO>(logits, geo.item(), L);
-#pragma unroll
-            for (int k = 0; k < K * N; ++k) L[k] *= kLog2e;
-            sinkhorn_sweep<N>(L, y);
-            softmax_rows<N, K>(L, y, T);
-            col_sums<N>(T, c);
-        }
-        ++it;
-        res = col_residual<N>(c);
-    }
+    newton_iterate<N, IO>(logits, geo.item(), tol, max_iter, T, y, c, res, it);
 #pragma unroll
     for (int k = 0; k < K * N; ++k) T_out[k] = T[k];
 #pragma unroll
@@ -653,6 +675,144 @@ newton_fwd_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, float* _
     const int it = newton_solve<N, IO>(geo, lds[geo.wave], logits, tol, max_iter, T, y, res);
     store_forward<N, IO>(geo, lds[geo.wave], Tout, dual, T, y);
     if (kStats && geo.valid() && geo.half() == 0) iters[geo.matrix()] = (res <= tol) ? it : -1;
+}
+
+// ---------------------------------------------------------------------------
+// Forward with the slow lanes gathered (n = 4, one matrix per lane).
+//
+// The number of Newton updates differs from matrix to matrix, and a wave runs
+// until its slowest lane is done; on inputs with a long tail (logits of large
+// magnitude) most lanes of a wave sit idle for most of its updates.  Here each
+// wave first runs at most kFirstPass updates and stores the matrices that are
+// done.  A wave with at most kHandOff lanes still running ("slow" lanes) hands
+// their state (T, dual, column sums) to the workgroup through its LDS region;
+// a wave with more keeps them.  After a workgroup barrier the waves that handed
+// off (or had nothing left) take the handed-off states 64 to a wave and carry
+// them on to tol or max_iter, while the rest exit, so that the updates of the
+// tail are spent on fewer waves.  Every matrix goes through exactly the updates
+// of newton_fwd_kernel from the same state, so the results are bit-identical.
+// ---------------------------------------------------------------------------
+constexpr int kFirstPass = 4;   // updates before the slow lanes are gathered
+constexpr int kHandOff = 32;    // most slow lanes a wave hands to the workgroup
+
+template <typename IO>
+struct Gather {
+    static constexpr int N = 4, M = N - 1, KN = Split<N>::K * N;
+    static_assert(Split<N>::R == 1, "one matrix per lane");
+    using G = Geometry<N, IO>;
+    // one handed-off state: T, y, c and the owner's lane in the workgroup; word j
+    // of record p sits at float j * kHandOff + p of the wave's region
+    static constexpr int kWords = KN + M + N + 1;
+    static constexpr int kRecordChunks = (kWords * kHandOff * 4 + 15) / 16;
+    static constexpr int kRegion = G::Tile::kLdsChunks > kRecordChunks ? G::Tile::kLdsChunks : kRecordChunks;
+};
+
+template <typename IO, bool kStats>
+__global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(7)))
+newton_fwd_gather_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, float* __restrict__ dual,
+                         int32_t* __restrict__ iters, int64_t B, float tol, int max_iter) {
+    using Q = Gather<IO>;
+    constexpr int N = Q::N, M = Q::M, KN = Q::KN;
+    using G = typename Q::G;
+    __shared__ uint4 lds[kWaves][Q::kRegion];
+    __shared__ int handed[kWaves];   // states a wave handed off; -1: it keeps its slow lanes
+    const G geo(B);
+    const int first = max_iter < kFirstPass ? max_iter : kFirstPass;
+    float T[KN], y[M], c[N], res = 0.0f;
+    int it = 0;
+    bool slow = false;
+    if (geo.nvalid > 0) {   // wave-uniform; waves past the end still reach the barrier
+        newton_start<N, IO>(geo, lds[geo.wave], logits, T, y, c, res);
+        newton_iterate<N, IO>(logits, geo.item(), tol, first, T, y, c, res, it);
+        slow = geo.valid() && res > tol && it < max_iter;
+        const uint64_t mask = __ballot(slow);
+        {
+            uint4 w[G::C];
+            Storage<IO>::template encode<KN>(T, w);
+            G::Tile::store_except(w, lds[geo.wave], geo.lane, geo.chunks(Tout), geo.nvalid * G::C, mask);
+        }
+        if (geo.valid() && !slow) {
+            float beta[N];
+#pragma unroll
+            for (int j = 0; j < M; ++j) beta[j] = y[j] * kLn2;
+            beta[M] = 0.0f;
+            store_dual<N>(dual, geo.matrix(), 0, beta);
+            if (kStats) iters[geo.matrix()] = (res <= tol) ? it : -1;
+        }
+        const int nslow = __popcll(mask);
+        if (nslow > 0 && nslow <= kHandOff) {
+            // the tile's last reads completed inside store_except; the region is free
+            float* rec = reinterpret_cast<float*>(lds[geo.wave]);
+            const int p = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+            if (slow) {
+#pragma unroll
+                for (int k = 0; k < KN; ++k) rec[k * kHandOff + p] = T[k];
+#pragma unroll
+                for (int j = 0; j < M; ++j) rec[(KN + j) * kHandOff + p] = y[j];
+#pragma unroll
+                for (int j = 0; j < N; ++j) rec[(KN + M + j) * kHandOff + p] = c[j];
+                rec[(KN + M + N) * kHandOff + p] = __int_as_float((int)threadIdx.x);
+            }
+            slow = false;   // carried on by the workgroup
+        }
+        if (geo.lane == 0) handed[geo.wave] = nslow > kHandOff ? -1 : nslow;
+    } else if (geo.lane == 0) {
+        handed[geo.wave] = 0;
+    }
+    __syncthreads();
+
+    // states handed off in the workgroup, and the waves before this one that take them
+    int total = 0, rank = 0;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+        const int h = handed[v];
+        total += h > 0 ? h : 0;
+        rank += (v < geo.wave && h >= 0) ? 1 : 0;
+    }
+    int64_t item = geo.item();
+    if (handed[geo.wave] >= 0) {
+        // a taking wave: handed-off state number t = rank * 64 + lane, if it exists
+        // (the takers are at least half as many as the waves that handed off, each of
+        // which handed off at most kHandOff <= 32 states, so all are taken)
+        if (rank * 64 >= total) return;
+        const int t = rank * 64 + geo.lane;
+        slow = t < total;
+        if (slow) {
+            int src = 0, p = t;
+#pragma unroll
+            for (int v = 0; v < kWaves - 1; ++v) {
+                const int h = handed[v] > 0 ? handed[v] : 0;
+                const bool past = src == v && p >= h;
+                p -= past ? h : 0;
+                src += past ? 1 : 0;
+            }
+            const float* rec = reinterpret_cast<const float*>(lds[src]);
+#pragma unroll
+            for (int k = 0; k < KN; ++k) T[k] = rec[k * kHandOff + p];
+#pragma unroll
+            for (int j = 0; j < M; ++j) y[j] = rec[(KN + j) * kHandOff + p];
+#pragma unroll
+            for (int j = 0; j < N; ++j) c[j] = rec[(KN + M + j) * kHandOff + p];
+            item = (int64_t)blockIdx.x * kBlock + __float_as_int(rec[(KN + M + N) * kHandOff + p]);
+            res = col_residual<N>(c);
+            it = first;
+        }
+    }
+    if (slow) {
+        newton_iterate<N, IO>(logits, item, tol, max_iter, T, y, c, res, it);
+        uint4 w[G::C];
+        Storage<IO>::template encode<KN>(T, w);
+        uint4* q = reinterpret_cast<uint4*>(Tout) + item * G::C;
+#pragma unroll
+        for (int k = 0; k < G::C; ++k) stream_store(q + k, w[k]);
+        float beta[N];
+#pragma unroll
+        for (int j = 0; j < M; ++j) beta[j] = y[j] * kLn2;
+        beta[M] = 0.0f;
+        store_dual<N>(dual, item, 0, beta);
+        if (kStats) iters[item] = (res <= tol) ? it : -1;
+    }
 }
 
 // ---------------------------------------------------------------------------

@@ -508,3 +508,71 @@ def test_near_singular_hessian_does_not_stall():
     T_ref, _, st = oracle.project(Hs.astype(np.float64), sk_cap=w.sk_cap)
     assert (st >= 0).all()
     check_forward(w, Hs.astype(np.float64), host_f64(T), dual.cpu().numpy().astype(np.float64), T_ref)
+
+
+# ------------------------------------- slow lanes gathered across the workgroup
+
+# Slow lanes (still running after the first four updates) per wave of 64, four
+# waves to a workgroup: hand-offs that fill one or two waves, waves that keep
+# their slow lanes (more than 32), mixtures, an idle workgroup, and a last
+# workgroup with a partial wave and two empty ones.
+GATHER_WAVES = [32, 32, 32, 32,
+                64, 0, 0, 1,
+                33, 32, 5, 64,
+                0, 0, 0, 0,
+                17, 63, 2, 32]
+GATHER_TAIL = (40, 20)   # a last wave of 40 matrices, 20 of them slow
+
+
+def gather_batch(seed=90):
+    """Logits laid out by GATHER_WAVES: "slow" matrices take >= 8 float64 Newton
+    updates in the oracle (N(0, 8^2) logits), "fast" ones <= 2 (N(0, 0.5^2) + 2I)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    pool = (rng.standard_normal((12000, 4, 4)) * 8.0).astype(np.float32)
+    _, _, it = oracle.newton(pool.astype(np.float64), tol=1e-6, max_iter=100)
+    slow = list(pool[it >= 8])
+    easy = (rng.standard_normal((4000, 4, 4)) * 0.5 + 2.0 * np.eye(4)).astype(np.float32)
+    _, _, it = oracle.newton(easy.astype(np.float64), tol=1e-6, max_iter=100)
+    fast = list(easy[(it >= 0) & (it <= 2)])
+    waves = [(64, s) for s in GATHER_WAVES] + [GATHER_TAIL]
+    out, want_slow = [], []
+    for size, s in waves:
+        pos = set(rng.choice(size, s, replace=False).tolist())
+        for lane in range(size):
+            out.append(slow.pop() if lane in pos else fast.pop())
+            want_slow.append(lane in pos)
+    return np.stack(out), np.array(want_slow)
+
+
+@pytest.mark.parametrize("max_iter", [100, 5, 4])
+def test_gathered_slow_lanes(max_iter):
+    """The n = 4 forward hands the slow lanes of a wave to other waves of its
+    workgroup: every layout of slow lanes gives the oracle's projection, and the
+    same T and dual, bit for bit, as the fused kernel (which runs every matrix to
+    the end in its own lane)."""
+    Hs, want_slow = gather_batch()
+    B = Hs.shape[0]
+    print("case gather B=%d max_iter=%d" % (B, max_iter), flush=True)
+    H = dev(Hs)
+    T = torch.empty_like(H)
+    dual = torch.empty((B, 4), device=DEV)
+    iters = torch.empty(B, dtype=torch.int32, device=DEV)
+    bp.birkhoff_fwd_ex(H, T, dual, iters, 1e-6, max_iter)
+    T2, d2, dH = torch.empty_like(H), torch.empty_like(dual), torch.empty_like(H)
+    bp.birkhoff_fwd_bwd(H, dev(np.ones_like(Hs)), T2, d2, dH, 1e-6, max_iter)
+    T3, d3 = torch.empty_like(H), torch.empty_like(dual)
+    bp.birkhoff_fwd(H, T3, d3, 1e-6, max_iter)
+    torch.cuda.synchronize()
+    assert torch.equal(T, T2) and torch.equal(dual, d2)
+    assert torch.equal(T, T3) and torch.equal(dual, d3)
+    it = iters.cpu().numpy()
+    assert ((it == -1) | ((it >= 0) & (it <= max_iter))).all()
+    if max_iter == 100:
+        # the layout is the intended one: slow matrices need more than 4 updates in fp32
+        assert (it >= 0).all()
+        np.testing.assert_array_equal(it > 4, want_slow)
+        T_ref, _, st = oracle.project(Hs.astype(np.float64))
+        assert (st >= 0).all()
+        check_forward(W.WORKLOADS["hard"], Hs.astype(np.float64), host_f64(T), None, T_ref)
+    else:
+        assert (it[~want_slow] >= 0).all()
