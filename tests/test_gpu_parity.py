@@ -515,12 +515,13 @@ def test_near_singular_hessian_does_not_stall():
 # Slow lanes (still running after the first four updates) per wave of 64, four
 # waves to a workgroup: hand-offs that fill one or two waves, waves that keep
 # their slow lanes (more than 32), mixtures, an idle workgroup, and a last
-# workgroup with a partial wave and two empty ones.
+# workgroup with a partial wave and three empty ones.
 GATHER_WAVES = [32, 32, 32, 32,
                 64, 0, 0, 1,
                 33, 32, 5, 64,
                 0, 0, 0, 0,
-                17, 63, 2, 32]
+                17, 63, 2, 21,
+                31, 33, 20, 1]
 GATHER_TAIL = (40, 20)   # a last wave of 40 matrices, 20 of them slow
 
 
