@@ -30,7 +30,8 @@ from . import build as hipbuild
 ROOT = pathlib.Path(__file__).resolve().parent.parent
 
 # device kernel -> the C-ABI entry point that launches it
-ENTRY = (("newton_fwd_kernel", "birkhoff_fwd"), ("implicit_bwd_from_T_kernel", "birkhoff_bwd_from_T"),
+ENTRY = (("newton_fwd_kernel", "birkhoff_fwd"), ("newton_fwd_gather_kernel", "birkhoff_fwd"),
+         ("implicit_bwd_from_T_kernel", "birkhoff_bwd_from_T"),
          ("implicit_bwd_kernel", "birkhoff_bwd"),
          ("sinkhorn_kernel", "sinkhorn_fwd"), ("fused_fwd_bwd_kernel", "birkhoff_fwd_bwd"),
          ("eot_fwd_kernel", "birkhoff_eot_fwd"), ("eot_bwd_kernel", "birkhoff_eot_bwd"),
@@ -47,7 +48,7 @@ def entry_of(kernel_name: str):
 
 def stats_variant(kernel_name: str) -> bool:
     """The forward kernels' variant that also writes iteration counts (template flag true)."""
-    return "fwd_kernel<" in kernel_name and "true>" in kernel_name
+    return ("fwd_kernel<" in kernel_name or "fwd_gather_kernel<" in kernel_name) and "true>" in kernel_name
 
 
 def one_csv(d: pathlib.Path, suffix: str) -> pathlib.Path:
