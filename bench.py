@@ -407,6 +407,82 @@ def forward_only_report(w, args, dev):
     }
 
 
+def pages_shape_report(args, dev):
+    """The pages' timing shape (Table 3 of the mHC projection paper, section 5):
+    4x4 fp32 logits ~ N(0, 10^2) at B in {512, ..., 131072}.  For each B, the
+    median over `--steps` single calls of the Newton forward, forward then
+    backward, the one-launch forward + backward and the 20-sweep Sinkhorn-Knopp
+    forward, each call timed alone with HIP events after the caches are flushed by
+    writing 1 GiB; plus the accuracy of the two forwards in float64 (max
+    residual and the L1 marginal error)."""
+    import statistics
+
+    import torch
+
+    import birkhoff_projection_amd as bp
+    from birkhoff_projection_amd import workloads as W
+
+    stream = torch.cuda.current_stream(dev)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+    rows = []
+    for B in W.PAGES_SHAPE_BATCHES:
+        w = W.pages_shape_workload(B)
+        H = torch.from_numpy(W.make_logits(w)).to(dev)
+        G = torch.from_numpy(W.make_upstream(w)).to(dev)
+        T, S, dH = torch.empty_like(H), torch.empty_like(H), torch.empty_like(H)
+        dual = torch.empty((B, 4), dtype=torch.float32, device=dev)
+        calls = {
+            "newton_fwd": lambda: bp.birkhoff_fwd(H, T, dual, w.tol, w.max_iter, stream),
+            "newton_fwd_then_bwd": lambda: (bp.birkhoff_fwd(H, T, dual, w.tol, w.max_iter, stream),
+                                            bp.birkhoff_bwd(H, dual, G, dH, stream)),
+            "newton_fwd_bwd_one_launch": lambda: bp.birkhoff_fwd_bwd(H, G, T, dual, dH, w.tol, w.max_iter, stream),
+            "sinkhorn20_fwd": lambda: bp.sinkhorn_fwd(H, S, 20, stream),
+        }
+        row = {"B": B}
+        for name, fn in calls.items():
+            for _ in range(5):
+                fn()
+            times = []
+            for _ in range(args.steps):
+                flush.fill_(1.0)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1) * 1e3)
+            row[name + "_us"] = statistics.median(times)
+        iters = torch.empty(B, dtype=torch.int32, device=dev)
+        bp.birkhoff_fwd_ex(H, T, dual, iters, w.tol, w.max_iter, stream)
+        bp.sinkhorn_fwd(H, S, 20, stream)
+        torch.cuda.synchronize()
+        for name, X in (("newton", T), ("sinkhorn20", S)):
+            Xd = X.double()
+            r = (Xd.sum(2) - 1).abs()
+            c = (Xd.sum(1) - 1).abs()
+            l1 = r.sum(1) + c.sum(1)
+            row[name + "_max_residual"] = torch.maximum(r.amax(1), c.amax(1)).max().item()
+            row[name + "_l1_median"] = l1.median().item()
+            row[name + "_l1_max"] = l1.max().item()
+        it = iters.cpu()
+        row["newton_iterations_mean"] = float(it[it >= 0].float().mean())
+        row["newton_unconverged"] = int((it < 0).sum())
+        rows.append(row)
+        print(json.dumps(row), file=sys.stderr, flush=True)
+    del flush
+    last = rows[-1]
+    return {
+        "metric": "median us per call, 4x4 fp32, H~N(0,10^2), cold caches (the pages' timing shape)",
+        "value": last["newton_fwd_then_bwd_us"], "unit": "us at B=%d (fwd then bwd)" % last["B"],
+        "n_gpus": 1, "steps": args.steps, "warmup": 5, "higher_is_better": False, "scaling": "none",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "pages_shape: 4x4 fp32, H~N(0,10^2), dT~N(0,1), B in %s, tol 1e-6, "
+                               "max_iter 100" % (list(W.PAGES_SHAPE_BATCHES),)},
+        "rows": rows,
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -435,13 +511,16 @@ def main() -> int:
     import birkhoff_projection_amd as bp
     from birkhoff_projection_amd import workloads as W
 
-    known = sorted(W.WORKLOADS) + sorted(W.EOT_WORKLOADS) + sorted(W.MIX_WORKLOADS)
+    known = sorted(W.WORKLOADS) + sorted(W.EOT_WORKLOADS) + sorted(W.MIX_WORKLOADS) + ["pages_shape"]
     if args.workload not in known:
         print("unknown workload %r (have %s)" % (args.workload, known), file=sys.stderr)
         return 2
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     bp.load_library()
+    if args.workload == "pages_shape":
+        print(json.dumps(pages_shape_report(args, dev)), flush=True)
+        return 0
     if args.workload in W.EOT_WORKLOADS:
         w = W.EOT_WORKLOADS[args.workload]
         out = eot_report(w, args, dev)

@@ -72,6 +72,17 @@ WORKLOADS = {
 }
 
 
+# The timing shape of the pages' Table 3 (section 5): 4x4 logits ~ N(0, 10^2) at
+# five batch sizes, forward and forward + backward.  A context report, not a
+# benchmark line: one workload per batch size, all from seed 8.
+PAGES_SHAPE_BATCHES = (512, 2048, 8192, 32768, 131072)
+
+
+def pages_shape_workload(B: int) -> Workload:
+    return Workload(key="shape%d" % B, title="4x4 fp32, B=%d, H~N(0,10^2), dT~N(0,1)" % B, B=B, n=4, io="f32",
+                    logits=("normal", 10.0), upstream=("normal", 1.0), passes="fwd+bwd", seed=8, max_iter=100,
+                    sk_cap=5_000)
+
 def _draw(recipe: Tuple, B: int, n: int, seed: int, m: Optional[int] = None) -> np.ndarray:
     """fp32 [B, n, m] (m defaults to n) values for a recipe (scaling done in float64, then rounded)."""
     rng = np.random.Generator(np.random.PCG64(seed))
