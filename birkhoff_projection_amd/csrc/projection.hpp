@@ -56,9 +56,12 @@ struct Pair<1> {
 
 template <>
 struct Pair<2> {
-    // the partner lane's value: DPP quad_perm [1,0,3,2] swaps lanes 2k and 2k+1
+    // the partner lane's value: DPP quad_perm [1,0,3,2] swaps lanes 2k and 2k+1.  Both
+    // lanes of a pair are always active together (they hold the same per-matrix
+    // state), so bound_ctrl changes no value; it lets the compiler fold the move
+    // into the consuming add or max (one v_add_f32_dpp instead of two instructions).
     __device__ __forceinline__ static float other(float v) {
-        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
     }
     __device__ __forceinline__ static float sum(float v) { return v + other(v); }
     __device__ __forceinline__ static float max(float v) { return fmaxf(v, other(v)); }

@@ -579,6 +579,32 @@ def test_gathered_slow_lanes(max_iter):
         assert (it[~want_slow] >= 0).all()
 
 
+
+@pytest.mark.parametrize("max_iter", [100, 5])
+def test_gathered_slow_lanes_bf16(max_iter):
+    """The same layouts in bf16 storage (the slow / fast split of the fp32 pool
+    mostly survives the rounding): the gathering forward's T and dual equal the
+    fused kernel's bit for bit and pass the bf16 gates against the oracle."""
+    Hf, _ = gather_batch()
+    Hs = W.f32_to_bf16_bits(Hf)
+    B = Hs.shape[0]
+    print("case gather bf16 B=%d max_iter=%d" % (B, max_iter), flush=True)
+    w = W.WORKLOADS["bw"]
+    H = dev(Hs).view(torch.bfloat16)
+    T = torch.empty_like(H)
+    dual = torch.empty((B, 4), device=DEV)
+    bp.birkhoff_fwd_bf16(H, T, dual, 1e-6, max_iter)
+    T2, d2, dH = torch.empty_like(H), torch.empty_like(dual), torch.empty_like(H)
+    G = dev(W.f32_to_bf16_bits(np.ones_like(Hf))).view(torch.bfloat16)
+    bp.birkhoff_fwd_bwd_bf16(H, G, T2, d2, dH, 1e-6, max_iter)
+    torch.cuda.synchronize()
+    assert torch.equal(T, T2) and torch.equal(dual, d2)
+    if max_iter == 100:
+        H64 = W.decode_f64(Hs)
+        T_ref, _, st = oracle.project(H64)
+        assert (st >= 0).all()
+        check_forward(w, H64, host_f64(T), dual.cpu().numpy().astype(np.float64), T_ref)
+
 def conditioned_backward_check(dH_gpu, dH_ref, T_ref):
     """Backward gate on inputs whose projection is close to a permutation.  dH
     depends on T through Delta^{-1} (eq 13), Delta = I - T_{-n}^T T_{-n}: an
