@@ -68,7 +68,7 @@ struct Vec<uint16_t> {
     __device__ __forceinline__ static uint4 encode(const float (&v)[V]) {
         uint32_t u[4];
 #pragma unroll
-        for (int h = 0; h < 4; ++h) u[h] = f32_to_bf16(v[2 * h]) | (f32_to_bf16(v[2 * h + 1]) << 16);
+        for (int h = 0; h < 4; ++h) u[h] = pack_bf16x2(v[2 * h], v[2 * h + 1]);
         return make_uint4(u[0], u[1], u[2], u[3]);
     }
 };
