@@ -1,8 +1,8 @@
 """Condense rocprofv3 CSV output into the short summaries kept under profiles/.
 
     python -m birkhoff_projection_amd.profile_summary --workload train \\
-        --stats gpurun_out/kt_train --fetch gpurun_out/pmc_fetch --write gpurun_out/pmc_write \\
-        --copy-mib 512 --cmd-stats "..." --cmd-fetch "..." --cmd-write "..." [--sq gpurun_out/pmc_sq --cmd-sq "..."]
+        --stats prof/kt_train --fetch prof/pmc_fetch --write prof/pmc_write \\
+        --copy-mib 512 --cmd-stats "..." --cmd-fetch "..." --cmd-write "..." [--sq prof/pmc_sq --cmd-sq "..."]
 
 Inputs are the directories rocprofv3 wrote with `--output-format csv`:
   --stats  a `--kernel-trace --stats` run (reads *_kernel_stats.csv);
