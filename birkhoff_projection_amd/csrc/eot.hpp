@@ -54,6 +54,17 @@ struct Items {
     static constexpr int kSteps = (kChunks + 63) / 64;
 
     __device__ __forceinline__ static int pos(int f) { return (f / F) * FP + f % F; }
+    // LDS position of float e (< 4) of 16-byte chunk c.  When an item is a whole
+    // number of chunks the four floats of a chunk belong to one item and sit side
+    // by side, so one division per chunk serves all four.
+    __device__ __forceinline__ static int chunk_pos(int c, int e) {
+        if constexpr (F % 4 == 0) {
+            constexpr int CI = F / 4;   // chunks per item
+            return (c / CI) * FP + 4 * (c % CI) + e;
+        } else {
+            return pos(4 * c + e);
+        }
+    }
 
     // `src` is the span's first float; `nf` (wave-uniform) floats of it exist.
     __device__ __forceinline__ static void load(const float* __restrict__ src, int nf, float* lds, int lane,
@@ -70,10 +81,10 @@ struct Items {
             for (int k = 0; k < kSteps; ++k) {
                 const int c = k * 64 + lane;
                 if ((k + 1) * 64 <= kChunks || c < kChunks) {
-                    lds[pos(4 * c + 0)] = __uint_as_float(t[k].x);
-                    lds[pos(4 * c + 1)] = __uint_as_float(t[k].y);
-                    lds[pos(4 * c + 2)] = __uint_as_float(t[k].z);
-                    lds[pos(4 * c + 3)] = __uint_as_float(t[k].w);
+                    lds[chunk_pos(c, 0)] = __uint_as_float(t[k].x);
+                    lds[chunk_pos(c, 1)] = __uint_as_float(t[k].y);
+                    lds[chunk_pos(c, 2)] = __uint_as_float(t[k].z);
+                    lds[chunk_pos(c, 3)] = __uint_as_float(t[k].w);
                 }
             }
         } else {
@@ -107,8 +118,8 @@ struct Items {
             for (int k = 0; k < kSteps; ++k) {
                 const int c = k * 64 + lane;
                 if ((k + 1) * 64 <= kChunks || c < kChunks) {
-                    const uint4 w = make_uint4(__float_as_uint(lds[pos(4 * c + 0)]), __float_as_uint(lds[pos(4 * c + 1)]),
-                                               __float_as_uint(lds[pos(4 * c + 2)]), __float_as_uint(lds[pos(4 * c + 3)]));
+                    const uint4 w = make_uint4(__float_as_uint(lds[chunk_pos(c, 0)]), __float_as_uint(lds[chunk_pos(c, 1)]),
+                                               __float_as_uint(lds[chunk_pos(c, 2)]), __float_as_uint(lds[chunk_pos(c, 3)]));
                     stream_store(d4 + c, w);
                 }
             }
