@@ -22,15 +22,23 @@ SOURCES = sorted(CSRC.glob("*.hip"))
 ARCH = "gfx950"
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source with comments, trailing blanks and empty lines removed (the
+    sources hold no string literal containing a comment marker)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_digest() -> str:
-    """Short hash of every device / ABI source file; identifies which kernels a
-    profile was taken on."""
+    """Short hash of the code (comments excluded) of every device / ABI source
+    file; identifies which kernels a profile was taken on."""
     import hashlib
     h = hashlib.sha256()
-    for p in sorted(list(CSRC.glob("*")) + [ROOT / "include" / "birkhoff.h"]):
-        if p.is_file():
-            h.update(p.name.encode())
-            h.update(p.read_bytes())
+    for p in sorted(list(CSRC.glob("*.hip")) + list(CSRC.glob("*.hpp")) + [ROOT / "include" / "birkhoff.h"]):
+        h.update(p.name.encode())
+        h.update(_code_only(p.read_text()).encode())
     return h.hexdigest()[:16]
 
 

@@ -5,18 +5,19 @@
 // each lane owning K = n / R of its rows: R = 1 for n = 4 (one matrix per
 // lane, 64 per wave; 16 entries of T and the 6-entry Hessian triangle per
 // lane) and R = 2 for n = 8 (a lane pair per matrix, 32 per wave, so that a
-// lane's share of T, the 28-entry Hessian and its Cholesky factor leave room
-// for four or more waves per SIMD).  Row-local work (softmaxes, row sums,
+// lane's share of T, the 28-entry Hessian and its Cholesky factor fit three
+// waves per SIMD without spilling).  Row-local work (softmaxes, row sums,
 // trial-point updates) stays in the owning lane; column sums and the Hessian's
 // dot products are completed with one DPP exchange inside the pair.  Both
 // lanes of a pair then hold bit-identical copies of every per-matrix quantity
 // (the exchange adds the two halves in either order, which is the same sum),
 // so the Newton solve and the step-size search run redundantly in both and
 // take identical decisions.  There is no MFMA: the work is tiny and
-// independent per matrix.  LDS is used only to make matrix loads and stores
-// coalesced wave-wide accesses (WaveTile) and, in the fused kernel, to land
-// dL/dT while the iteration runs.  Control flow is per lane (per pair); the
-// wave keeps stepping while any of its matrices is unconverged.
+// independent per matrix.  LDS is used to make matrix loads and stores
+// coalesced wave-wide accesses (WaveTile), in the fused kernel to land dL/dT
+// while the iteration runs, and in the n = 4 forward to hand slow lanes to
+// other waves of the workgroup.  Control flow is per lane (per pair); a wave
+// keeps stepping while any of its matrices is unconverged.
 //
 // Units.  Logits are scaled by log2(e) on load and the dual is kept in the
 // same base-2 units (y = beta * log2 e), so that every exponential is one
