@@ -653,3 +653,50 @@ def test_parity_pages_timing_shape(B):
     rel2, rel2_wc = conditioned_backward_check(host_f64(dH2), dH_ref, T_ref)
     print("  max updates %d, fwd err %.2e, residual %.2e, bwd rel %.2e / fused %.2e "
           "(where lambda_min > 0.1: %.2e / %.2e)" % (it.max(), err, res, rel, rel2, rel_wc, rel2_wc))
+
+
+@pytest.mark.parametrize("B", [1, 65, 257, 1000, 1320])
+def test_gathered_ragged_batches_and_canaries(B):
+    """Slow matrices (the gathered path's per-lane stores) in ragged batches: every
+    output lands in its slot and the padding around each buffer keeps its sentinel."""
+    print("case gather ragged", B, flush=True)
+    Hs = gather_batch()[0][:B]
+    pad, sentinel = 3, 12345.0
+    Tbuf = torch.full((B + 2 * pad, 4, 4), sentinel, device=DEV)
+    Dbuf = torch.full((B + 2 * pad, 4), sentinel, device=DEV)
+    Ibuf = torch.full((B + 2 * pad,), -7, dtype=torch.int32, device=DEV)
+    T, dual, it = Tbuf[pad:pad + B], Dbuf[pad:pad + B], Ibuf[pad:pad + B]
+    bp.birkhoff_fwd_ex(dev(Hs), T, dual, it, 1e-6, 100)
+    torch.cuda.synchronize()
+    for buf in (Tbuf, Dbuf):
+        assert (buf[:pad] == sentinel).all() and (buf[pad + B:] == sentinel).all()
+    assert (Ibuf[:pad] == -7).all() and (Ibuf[pad + B:] == -7).all()
+    assert (it.cpu().numpy() >= 0).all()
+    T_ref, _, _ = oracle.project(Hs.astype(np.float64))
+    check_forward(W.WORKLOADS["hard"], Hs.astype(np.float64), host_f64(T), None, T_ref)
+
+
+def test_gathered_nonfinite_inputs_stay_in_their_matrix():
+    """Non-finite logits among slow matrices: the bad matrices end with count -1 and
+    every other matrix's T and dual are those of the clean batch, bit for bit."""
+    Hs, want_slow = gather_batch()
+    bad = Hs.copy()
+    slow_idx = np.flatnonzero(want_slow)
+    hit = [int(slow_idx[3]), int(slow_idx[40]), 7, int(slow_idx[200])]
+    bad[hit[0], 1, 2] = np.nan
+    bad[hit[1], 0, 0] = np.inf
+    bad[hit[2], 2, 1] = np.nan
+    bad[hit[3], 3, 3] = np.inf
+    B = Hs.shape[0]
+    out = []
+    for X in (Hs, bad):
+        T = torch.empty((B, 4, 4), device=DEV)
+        d = torch.empty((B, 4), device=DEV)
+        it = torch.empty(B, dtype=torch.int32, device=DEV)
+        bp.birkhoff_fwd_ex(dev(X), T, d, it, 1e-6, 100)
+        out.append((T.cpu().numpy(), d.cpu().numpy(), it.cpu().numpy()))
+    keep = np.setdiff1d(np.arange(B), hit)
+    assert np.array_equal(out[0][0][keep], out[1][0][keep])
+    assert np.array_equal(out[0][1][keep], out[1][1][keep])
+    assert np.array_equal(out[0][2][keep], out[1][2][keep])
+    assert (out[1][2][hit] == -1).all()
