@@ -8,7 +8,10 @@ the training-shaped mHC pass -- B = 16 sequences x 4096 tokens x 32 layers =
 dL/dT = N(0, 0.1^2), tol 1e-6 -- whose forward and backward are fused.  The
 timed step is therefore one birkhoff_fwd_bwd launch (--path fused, default);
 --path separate times birkhoff_fwd followed by birkhoff_bwd instead.  Either
-way the other form is timed too and reported under "other_path".
+way the other form is timed too and reported under "other_path", and the
+timed step is also captured into a HIP graph and replayed ("graph_replay":
+the same kernels without the host's launch work between them, which is what
+decides the small, launch-bound workload).
 
 Inputs are generated on the host from fixed seeds and copied to HBM before
 anything is timed.  Two complete input/output sets alternate between steps, so
@@ -549,6 +552,39 @@ def main() -> int:
     return 0
 
 
+def graph_replay(step, sets, K, dev):
+    """ms per step when the steps are captured into a HIP graph (torch.cuda.CUDAGraph,
+    50 steps per graph) and replayed: the same kernels without the host's per-launch
+    work between them, as a caller that captures its step would run them.  `step`
+    must launch on the current stream."""
+    import torch
+
+    per = min(K, 50)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        for i in range(3):
+            step(sets[i % 2])
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(per):
+            step(sets[i % 2])
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, K // per)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * per)
+    del g
+    return ms
+
 def forward_backward_report(w, args, dev):
     """The forward + backward workloads: the timed step is the fused launch or
     the two separate launches (--path); the other form is timed too."""
@@ -619,6 +655,15 @@ def forward_backward_report(w, args, dev):
     bwd_ms = timed(run_bwd, K)
     fused_ms = ms_step if args.path == "fused" else ms_other
 
+    def step_on_current(s):   # the same step, launched on whatever stream is current
+        if args.path == "fused":
+            fused(s["H"], s["G"], s["T"], s["dual"], s["dH"], w.tol, w.max_iter)
+        else:
+            fwd(s["H"], s["T"], s["dual"], w.tol, w.max_iter)
+            bwd(s["H"], s["dual"], s["G"], s["dH"])
+
+    ms_graph = graph_replay(step_on_current, sets, K, dev)
+
     b_fwd = W.bytes_per_projection(n, w.io, "fwd") * B
     b_bwd = W.bytes_per_projection(n, w.io, "bwd") * B
     b_fused = W.bytes_per_projection(n, w.io, "fused") * B
@@ -655,6 +700,7 @@ def forward_backward_report(w, args, dev):
                      "frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "other_path": {"path": "separate" if args.path == "fused" else "fused", "ms_per_step": ms_other,
                        "value": B / (ms_other * 1e-3)},
+        "graph_replay": {"path": args.path, "ms_per_step": ms_graph, "value": B / (ms_graph * 1e-3)},
         "kernel_digest": digest,
     }
     return out

@@ -700,3 +700,45 @@ def test_gathered_nonfinite_inputs_stay_in_their_matrix():
     assert np.array_equal(out[0][1][keep], out[1][1][keep])
     assert np.array_equal(out[0][2][keep], out[1][2][keep])
     assert (out[1][2][hit] == -1).all()
+
+
+def test_graph_capture_and_replay():
+    """The entry points launch on the stream they are given, allocate nothing and
+    record no memset, so a step can be captured into a HIP graph: every replay,
+    with the program's own eager work and synchronisations in between, gives the
+    eager results bit for bit."""
+    w = W.WORKLOADS["pr1"]
+    Hs, Gs = W.make_logits(w), W.make_upstream(w)
+    H, G = dev(Hs), dev(Gs)
+    B = Hs.shape[0]
+    T0, d0, dH0 = torch.empty_like(H), torch.empty((B, 4), device=DEV), torch.empty_like(H)
+    bp.birkhoff_fwd_bwd(H, G, T0, d0, dH0, w.tol, w.max_iter)
+    T1, d1, dH1 = torch.empty_like(H), torch.empty((B, 4), device=DEV), torch.empty_like(H)
+    dH2 = torch.empty_like(H)
+    Tf, df = torch.empty_like(H), torch.empty((B, 4), device=DEV)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        bp.birkhoff_fwd_bwd(H, G, T1, d1, dH1, w.tol, w.max_iter)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        bp.birkhoff_fwd_bwd(H, G, T1, d1, dH1, w.tol, w.max_iter)
+        bp.birkhoff_fwd(H, Tf, df, w.tol, w.max_iter)
+        bp.birkhoff_bwd(H, df, G, dH2)
+    T_e, d_e = torch.empty_like(H), torch.empty((B, 4), device=DEV)
+    bp.birkhoff_fwd(H, T_e, d_e, w.tol, w.max_iter)
+    dH_e = torch.empty_like(H)
+    bp.birkhoff_bwd(H, d_e, G, dH_e)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in (T1, d1, dH1, Tf, df, dH2):
+            t.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(T1, T0) and torch.equal(d1, d0) and torch.equal(dH1, dH0), rep
+        assert torch.equal(Tf, T_e) and torch.equal(df, d_e) and torch.equal(dH2, dH_e), rep
+        bp.project(H)   # eager work between replays
+        torch.cuda.synchronize()
