@@ -106,17 +106,21 @@ __device__ __forceinline__ void softmax_rows(const float (&L)[K * N], const floa
     }
 }
 
-// softmax_rows at beta = 0 (the starting point x^(0) = 0)
+// softmax_rows at beta = 0 (the starting point x^(0) = 0), from logits H in
+// natural units.  The row maximum is taken before the scaling by log2 e: a
+// positive scale keeps the order and rounding is monotone, so it is the
+// maximum of the scaled row; each exponent is then one fma, H log2 e - mu.
 template <int N, int K>
-__device__ __forceinline__ void softmax_rows0(const float (&L)[K * N], float (&T)[K * N]) {
+__device__ __forceinline__ void softmax_rows0(const float (&H)[K * N], float (&T)[K * N]) {
 #pragma unroll
     for (int i = 0; i < K; ++i) {
-        float mu = L[i * N];
+        float mu = H[i * N];
 #pragma unroll
-        for (int j = 1; j < N; ++j) mu = fmaxf(mu, L[i * N + j]);
+        for (int j = 1; j < N; ++j) mu = fmaxf(mu, H[i * N + j]);
+        mu *= kLog2e;
         float u[N];
 #pragma unroll
-        for (int j = 0; j < N; ++j) u[j] = ex2(L[i * N + j] - mu);
+        for (int j = 0; j < N; ++j) u[j] = ex2(fmaf(H[i * N + j], kLog2e, -mu));
         float s = u[0];
 #pragma unroll
         for (int j = 1; j < N; ++j) s += u[j];
@@ -129,6 +133,9 @@ __device__ __forceinline__ void softmax_rows0(const float (&L)[K * N], float (&T
 // column sums c_j = sum_i T_ij (eq 11); the gradient of the reduced dual is c_{-n} - 1 (eq 9)
 template <int N>
 __device__ __forceinline__ void col_sums(const float (&T)[Split<N>::K * N], float (&c)[N]) {
+    // plain adds: T is held anyway, and fusing the products that formed it into
+    // these sums would compute every product twice
+#pragma clang fp contract(off)
     constexpr int K = Split<N>::K;
 #pragma unroll
     for (int j = 0; j < N; ++j) {
@@ -153,42 +160,43 @@ __device__ __forceinline__ float col_residual(const float (&c)[N]) {
 
 // Hessian of the reduced dual objective, eq (9) with eta = 1, a = b = 1:
 //   h_jk = [j == k] c_j - sum_i T_ij T_ik,   j, k < N-1.
-// The diagonal is evaluated as sum_i T_ij * (sum_{k != j} T_ik), which equals
-// c_j - sum_i T_ij^2 when every row of T sums to one but has no cancellation
-// when a column is dominated by one entry close to 1.  At the optimum this is
-// also the Delta of eq (13) ([P] section 4.2).
+// With the column Gram sums G_jk = sum_i T_ij T_ik (all N columns), the
+// diagonal is evaluated as sum_{k != j} G_jk.  When every row of T sums to one
+// this equals c_j - sum_i T_ij^2 (it is sum_i T_ij * (sum_{k != j} T_ik) with
+// the two sums swapped), but it adds only non-negative terms, so it has no
+// cancellation when a column is dominated by one entry close to 1; and the
+// off-diagonal sums are the ones h needs anyway.  At the optimum this is also
+// the Delta of eq (13) ([P] section 4.2).
 template <int N>
 __device__ __forceinline__ void hessian(const float (&T)[Split<N>::K * N], float (&h)[Tri<N>::S]) {
     constexpr int M = N - 1, K = Split<N>::K;
     using P = Pair<Split<N>::R>;
+    // this lane's share of G_jk (k < j < M) and of G_jM
+    float g[Tri<N>::S], gm[M];
 #pragma unroll
-    for (int j = 0; j < M; ++j)
+    for (int j = 0; j < M; ++j) {
 #pragma unroll
         for (int k = 0; k < j; ++k) {
             float p = T[j] * T[k];
 #pragma unroll
             for (int i = 1; i < K; ++i) p = fmaf(T[i * N + j], T[i * N + k], p);
-            h[Tri<N>::at(j, k)] = -P::sum(p);
+            g[Tri<N>::at(j, k)] = p;
         }
-    float dg[M];
+        float q = T[j] * T[M];
 #pragma unroll
-    for (int i = 0; i < K; ++i) {
-        // o_j = sum of row i without entry j, from prefix and suffix sums
-        float pre[N], suf[N];   // pre[k] = T_i0 + .. + T_i,k-1 (k >= 1); suf[k] = T_i,k+1 + .. (k <= N-2)
-        pre[1] = T[i * N];
-#pragma unroll
-        for (int k = 2; k < N; ++k) pre[k] = pre[k - 1] + T[i * N + k - 1];
-        suf[N - 2] = T[i * N + N - 1];
-#pragma unroll
-        for (int k = N - 3; k >= 0; --k) suf[k] = suf[k + 1] + T[i * N + k + 1];
-#pragma unroll
-        for (int j = 0; j < M; ++j) {
-            const float o = (j == 0) ? suf[0] : pre[j] + suf[j];
-            dg[j] = (i == 0) ? T[j] * o : fmaf(T[i * N + j], o, dg[j]);
-        }
+        for (int i = 1; i < K; ++i) q = fmaf(T[i * N + j], T[i * N + M], q);
+        gm[j] = q;
     }
 #pragma unroll
-    for (int j = 0; j < M; ++j) h[Tri<N>::at(j, j)] = P::sum(dg[j]);
+    for (int j = 0; j < M; ++j) {
+        float d = gm[j];
+#pragma unroll
+        for (int k = 0; k < M; ++k)
+            if (k != j) d += g[k < j ? Tri<N>::at(j, k) : Tri<N>::at(k, j)];
+        h[Tri<N>::at(j, j)] = P::sum(d);
+#pragma unroll
+        for (int k = 0; k < j; ++k) h[Tri<N>::at(j, k)] = -P::sum(g[Tri<N>::at(j, k)]);
+    }
 }
 
 // Adds 2^-22 tr(H) to the diagonal of the Newton system.  When some column of
@@ -577,13 +585,11 @@ __device__ __forceinline__ void newton_start(const Geometry<N, IO>& geo, uint4* 
     constexpr int M = N - 1, K = Split<N>::K;
     using G = Geometry<N, IO>;
     {
-        float L[K * N];
+        float H[K * N];
         uint4 w[G::C];
         G::Tile::load(geo.chunks(logits), geo.nvalid * G::C, lds, geo.lane, w);
-        Storage<IO>::template decode<K * N>(w, L);
-#pragma unroll
-        for (int k = 0; k < K * N; ++k) L[k] *= kLog2e;
-        softmax_rows0<N, K>(L, T);
+        Storage<IO>::template decode<K * N>(w, H);
+        softmax_rows0<N, K>(H, T);
     }
     // optionally start copying another tile of the wave (dL/dT) into the now
     // free LDS region, to be read after the iteration
@@ -601,22 +607,25 @@ __device__ __forceinline__ void newton_start(const Geometry<N, IO>& geo, uint4* 
         bool ok = true;
 #pragma unroll
         for (int j = 0; j < N; ++j) ok = ok && c[j] > 1.17549435e-38f && c[j] < 3.0e38f;
-        float rc[N];
+        if (ok) {
+            float rc[N];
 #pragma unroll
-        for (int j = 0; j < N; ++j) rc[j] = ok ? rcp(c[j]) : 1.0f;
+            for (int j = 0; j < N; ++j) rc[j] = rcp(c[j]);
 #pragma unroll
-        for (int j = 0; j < M; ++j) y[j] += ok ? lg2(c[N - 1] * rc[j]) : 0.0f;
+            for (int j = 0; j < M; ++j) y[j] += lg2(c[N - 1] * rc[j]);
 #pragma unroll
-        for (int i = 0; i < K; ++i) {
-            float rs = 0.0f;
+            for (int i = 0; i < K; ++i) {
+#pragma clang fp contract(off)
+                // (plain adds of the scaled entries, which are kept)
 #pragma unroll
-            for (int j = 0; j < N; ++j) {
-                T[i * N + j] *= rc[j];
-                rs += T[i * N + j];
+                for (int j = 0; j < N; ++j) T[i * N + j] *= rc[j];
+                float rs = T[i * N];
+#pragma unroll
+                for (int j = 1; j < N; ++j) rs += T[i * N + j];
+                const float r = rcp(rs);
+#pragma unroll
+                for (int j = 0; j < N; ++j) T[i * N + j] *= r;
             }
-            const float r = rcp(rs);
-#pragma unroll
-            for (int j = 0; j < N; ++j) T[i * N + j] *= r;
         }
     }
     col_sums<N>(T, c);
