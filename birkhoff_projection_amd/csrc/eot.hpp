@@ -176,10 +176,12 @@ __device__ __forceinline__ float col_residual(const float (&c)[M], const float (
 }
 
 // eta times the Hessian of eq (9): h_jk = [j == k] c_j - sum_i a_i S_ij S_ik,
-// j, k < m - 1.  The diagonal is formed as sum_i a_i S_ij (sum_{k != j} S_ik)
-// (equal to c_j - sum_i a_i S_ij^2 since rows of S sum to one), which does not
-// cancel when a column is carried by one entry.  At the optimum this is also
-// eq (13)'s Delta ([P] section 4.2).
+// j, k < m - 1.  With the weighted column Gram sums G_jk = sum_i a_i S_ij S_ik
+// (all m columns), the diagonal is formed as sum_{k != j} G_jk: the same
+// non-negative terms as sum_i a_i S_ij (sum_{k != j} S_ik), which equals
+// c_j - sum_i a_i S_ij^2 since rows of S sum to one, so it does not cancel when a
+// column is carried by one entry; the off-diagonal sums are reused.  At the
+// optimum this is also eq (13)'s Delta ([P] section 4.2).
 template <int N, int M>
 __device__ __forceinline__ void hessian(const float (&S)[N * M], const float (&a)[N], float (&h)[Tri<M>::S]) {
     constexpr int K1 = M - 1;
@@ -188,33 +190,30 @@ __device__ __forceinline__ void hessian(const float (&S)[N * M], const float (&a
     for (int i = 0; i < N; ++i)
 #pragma unroll
         for (int j = 0; j < K1; ++j) aS[i * K1 + j] = a[i] * S[i * M + j];
+    float g[Tri<M>::S], gm[K1];   // G_jk (k < j < m-1) and G_j,m-1
 #pragma unroll
-    for (int j = 0; j < K1; ++j)
+    for (int j = 0; j < K1; ++j) {
 #pragma unroll
         for (int k = 0; k < j; ++k) {
             float p = aS[j] * S[k];
 #pragma unroll
             for (int i = 1; i < N; ++i) p = fmaf(aS[i * K1 + j], S[i * M + k], p);
+            g[Tri<M>::at(j, k)] = p;
             h[Tri<M>::at(j, k)] = -p;
         }
-    float dg[K1];
+        float q = aS[j] * S[K1];
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-        float pre[M], suf[M];   // pre[k] = S_i0 + .. + S_i,k-1 (k >= 1); suf[k] = S_i,k+1 + .. (k <= M-2)
-        pre[1] = S[i * M];
-#pragma unroll
-        for (int k = 2; k < M; ++k) pre[k] = pre[k - 1] + S[i * M + k - 1];
-        suf[M - 2] = S[i * M + M - 1];
-#pragma unroll
-        for (int k = M - 3; k >= 0; --k) suf[k] = suf[k + 1] + S[i * M + k + 1];
-#pragma unroll
-        for (int j = 0; j < K1; ++j) {
-            const float o = (j == 0) ? suf[0] : pre[j] + suf[j];
-            dg[j] = (i == 0) ? aS[j] * o : fmaf(aS[i * K1 + j], o, dg[j]);
-        }
+        for (int i = 1; i < N; ++i) q = fmaf(aS[i * K1 + j], S[i * M + K1], q);
+        gm[j] = q;
     }
 #pragma unroll
-    for (int j = 0; j < K1; ++j) h[Tri<M>::at(j, j)] = dg[j];
+    for (int j = 0; j < K1; ++j) {
+        float d = gm[j];
+#pragma unroll
+        for (int k = 0; k < K1; ++k)
+            if (k != j) d += g[k < j ? Tri<M>::at(j, k) : Tri<M>::at(k, j)];
+        h[Tri<M>::at(j, j)] = d;
+    }
 }
 
 // e^x - 1 and e^x - 1 - x (the latter of second order in x) from one Taylor
@@ -433,12 +432,13 @@ eot_fwd_kernel(const float* __restrict__ cost, const float* __restrict__ a_in, c
         for (int j = 0; j < K1; ++j) y[j] = ok ? y[j] + lg2(f[j] * rf) : y[j];
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-            float rs = 0.0f;
+#pragma clang fp contract(off)
+            // (plain adds of the scaled entries, which are kept)
 #pragma unroll
-            for (int j = 0; j < M; ++j) {
-                S[i * M + j] *= f[j];
-                rs += S[i * M + j];
-            }
+            for (int j = 0; j < M; ++j) S[i * M + j] *= f[j];
+            float rs = S[i * M];
+#pragma unroll
+            for (int j = 1; j < M; ++j) rs += S[i * M + j];
             const float r = rcp(rs);
 #pragma unroll
             for (int j = 0; j < M; ++j) S[i * M + j] *= r;
