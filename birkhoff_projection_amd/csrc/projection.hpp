@@ -597,22 +597,36 @@ __device__ __forceinline__ void newton_start(const Geometry<N, IO>& geo, uint4* 
     // start: the dual after kStartSweeps Sinkhorn-Knopp sweeps from v = 1.  The
     // rows of exp(H) are normalised above (T at beta = 0); each sweep scales the
     // columns of T to sum to one and normalises the rows again, which moves the
-    // dual by beta_j += log c_{n-1} - log c_j.  A sweep whose column sums are 0 or
-    // not finite is skipped.
+    // dual by beta_j += log c_{n-1} - log c_j.  The sweeps are skipped when a
+    // column sum of this T is 0 or not finite: rows sum to one, so a column sum
+    // is at most n or NaN, and one comparison per column (false for NaN) decides.
+    // After one sweep no later sweep can fail that test: every column of
+    // T diag(1/c) sums to one, so it has an entry >= 1/n, and no row of it sums to
+    // more than n (each entry T_ij / c_j is at most 1), so every column sum of
+    // the renormalised T is at least 1/n^2.  For the same reason the later
+    // sweeps' ratios c_{n-1} / c_j lie within [n^-3, n^3]; their product is
+    // formed and its logarithm taken once.
+    static_assert(kStartSweeps >= 1, "the start has at least one sweep");
 #pragma unroll
     for (int j = 0; j < M; ++j) y[j] = 0.0f;
+    col_sums<N>(T, c);
+    bool ok = true;
 #pragma unroll
-    for (int sw = 0; sw < kStartSweeps; ++sw) {
-        col_sums<N>(T, c);
-        bool ok = true;
+    for (int j = 0; j < N; ++j) ok = ok && c[j] > 1.17549435e-38f;
+    if (ok) {
+        float q[M];   // product of the later sweeps' ratios
 #pragma unroll
-        for (int j = 0; j < N; ++j) ok = ok && c[j] > 1.17549435e-38f && c[j] < 3.0e38f;
-        if (ok) {
+        for (int sw = 0; sw < kStartSweeps; ++sw) {
+            if (sw > 0) col_sums<N>(T, c);
             float rc[N];
 #pragma unroll
             for (int j = 0; j < N; ++j) rc[j] = rcp(c[j]);
 #pragma unroll
-            for (int j = 0; j < M; ++j) y[j] += lg2(c[N - 1] * rc[j]);
+            for (int j = 0; j < M; ++j) {
+                const float ratio = c[N - 1] * rc[j];
+                if (sw == 0) y[j] = lg2(ratio);
+                else q[j] = (sw == 1) ? ratio : q[j] * ratio;
+            }
 #pragma unroll
             for (int i = 0; i < K; ++i) {
 #pragma clang fp contract(off)
@@ -627,6 +641,9 @@ __device__ __forceinline__ void newton_start(const Geometry<N, IO>& geo, uint4* 
                 for (int j = 0; j < N; ++j) T[i * N + j] *= r;
             }
         }
+        if constexpr (kStartSweeps > 1)
+#pragma unroll
+            for (int j = 0; j < M; ++j) y[j] += lg2(q[j]);
     }
     col_sums<N>(T, c);
     res = geo.valid() ? col_residual<N>(c) : 0.0f;   // lanes past the end are done
