@@ -220,7 +220,12 @@ __device__ __forceinline__ void damp(float (&h)[Tri<N>::S]) {
 // x = H^{-1} r for the symmetric positive definite (N-1) x (N-1) matrix H.
 // N = 4: the closed-form adjugate of eq (12).  Other N: Cholesky H = L L^T in
 // registers.  Returns false when H is not numerically positive definite (a
-// non-positive or non-finite determinant / pivot); x is then meaningless.
+// non-positive or non-finite determinant / pivot); x is then meaningless.  The
+// Hessians solved here have bounded entries (at most n for the Birkhoff
+// kernels, whose T lies in [0, 1]; at most the total of the marginals a in the
+// general problem), so for finite inputs a pivot or the determinant is finite
+// or NaN, and one comparison with the smallest normal number (false for NaN)
+// decides.
 template <int N>
 struct SpdSolve {
     __device__ __forceinline__ static bool run(const float (&h)[Tri<N>::S], const float (&r)[N - 1], float (&x)[N - 1]) {
@@ -233,7 +238,7 @@ struct SpdSolve {
             float s = h[Tri<N>::at(j, j)];
 #pragma unroll
             for (int k = 0; k < j; ++k) s = fmaf(-l[Tri<N>::at(j, k)], l[Tri<N>::at(j, k)], s);
-            ok = ok && (s > 1.17549435e-38f) && (s < 3.0e38f);
+            ok = ok && (s > 1.17549435e-38f);
             const float ri = rsq(s);
             dinv[j] = ri;
             l[Tri<N>::at(j, j)] = s * ri;
@@ -281,7 +286,7 @@ struct SpdSolve<4> {
         x[0] = fmaf(a11, r[0], fmaf(a12, r[1], a13 * r[2])) * q;
         x[1] = fmaf(a12, r[0], fmaf(a22, r[1], a23 * r[2])) * q;
         x[2] = fmaf(a13, r[0], fmaf(a23, r[1], a33 * r[2])) * q;
-        return (det > 1.17549435e-38f) && (det < 3.0e38f);
+        return det > 1.17549435e-38f;
     }
 };
 
