@@ -606,11 +606,10 @@ __device__ __forceinline__ void newton_start(const Geometry<N, IO>& geo, uint4* 
     // column sum of this T is 0 or not finite: rows sum to one, so a column sum
     // is at most n or NaN, and one comparison per column (false for NaN) decides.
     // After one sweep no later sweep can fail that test: every column of
-    // T diag(1/c) sums to one, so it has an entry >= 1/n, and no row of it sums to
-    // more than n (each entry T_ij / c_j is at most 1), so every column sum of
-    // the renormalised T is at least 1/n^2.  For the same reason the later
-    // sweeps' ratios c_{n-1} / c_j lie within [n^-3, n^3]; their product is
-    // formed and its logarithm taken once.
+    // T diag(1/c) sums to one and no row of it sums to more than n (each entry
+    // T_ij / c_j is at most 1), so every column sum of the renormalised T is at
+    // least 1/n.  The later sweeps' ratios c_{n-1} / c_j therefore lie within
+    // [n^-2, n^2]; their product is formed and its logarithm taken once.
     static_assert(kStartSweeps >= 1, "the start has at least one sweep");
 #pragma unroll
     for (int j = 0; j < M; ++j) y[j] = 0.0f;
