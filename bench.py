@@ -34,7 +34,7 @@ kernels have changed since.
 The CPU baseline is the float64 oracle timed on a bounded sample of the same
 workload on this host's cores.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload train] [--path fused|separate]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 300] [--workload train] [--path fused|separate]
 """
 from __future__ import annotations
 
