@@ -163,15 +163,13 @@ __device__ __forceinline__ void col_sums(const float (&S)[N * M], const float (&
     }
 }
 
-// max_j |c_j - b_j|; NaN propagates
+// max_j |c_j - b_j|; NaN propagates (IEEE 754-2019 `maximum`, gfx950's
+// v_maximum3_f32)
 template <int M>
 __device__ __forceinline__ float col_residual(const float (&c)[M], const float (&b)[M]) {
     float r = fabsf(c[0] - b[0]);
 #pragma unroll
-    for (int j = 1; j < M; ++j) {
-        const float e = fabsf(c[j] - b[j]);
-        r = (e > r || e != e) ? e : r;
-    }
+    for (int j = 1; j < M; ++j) r = __builtin_elementwise_maximum(r, fabsf(c[j] - b[j]));
     return r;
 }
 

@@ -110,13 +110,15 @@ __device__ __forceinline__ void softmax_rows(const float (&L)[K * N], const floa
 // natural units.  The row maximum is taken before the scaling by log2 e: a
 // positive scale keeps the order and rounding is monotone, so it is the
 // maximum of the scaled row; each exponent is then one fma, H log2 e - mu.
+// The maximum is IEEE 754-2019 `maximum` (gfx950's v_maximum3_f32, NaN
+// propagating), which needs no quieting of the freshly loaded values first.
 template <int N, int K>
 __device__ __forceinline__ void softmax_rows0(const float (&H)[K * N], float (&T)[K * N]) {
 #pragma unroll
     for (int i = 0; i < K; ++i) {
         float mu = H[i * N];
 #pragma unroll
-        for (int j = 1; j < N; ++j) mu = fmaxf(mu, H[i * N + j]);
+        for (int j = 1; j < N; ++j) mu = __builtin_elementwise_maximum(mu, H[i * N + j]);
         mu *= kLog2e;
         float u[N];
 #pragma unroll
@@ -146,15 +148,13 @@ __device__ __forceinline__ void col_sums(const float (&T)[Split<N>::K * N], floa
     }
 }
 
-// max_j |c_j - 1| over all N columns; NaN propagates
+// max_j |c_j - 1| over all N columns; NaN propagates (IEEE 754-2019
+// `maximum`, gfx950's v_maximum3_f32)
 template <int N>
 __device__ __forceinline__ float col_residual(const float (&c)[N]) {
     float r = fabsf(c[0] - 1.0f);
 #pragma unroll
-    for (int j = 1; j < N; ++j) {
-        const float e = fabsf(c[j] - 1.0f);
-        r = (e > r || e != e) ? e : r;
-    }
+    for (int j = 1; j < N; ++j) r = __builtin_elementwise_maximum(r, fabsf(c[j] - 1.0f));
     return r;
 }
 
