@@ -211,6 +211,7 @@ def eot_report(w, args, dev):
         "config": {"workload": "%s: %s" % (w.key, w.title), "B": B, "n": n, "m": m, "eta": w.eta,
                    "shared_marginals": w.shared, "passes": "fwd+bwd", "tol": w.tol, "max_iter": w.max_iter},
         "roofline": roofline(w.key, dom, d_bytes, d_ms, digest),
+        "copy_ref": copy_reference(d_bytes, d_bytes / (d_ms * 1e-3) / 1e9, dev),
         "kernels_ms": {"birkhoff_eot_fwd": fwd_ms, "birkhoff_eot_bwd": bwd_ms},
         "kernels_hbm_frac": {k: v[1] / (v[0] * 1e-3) / 1e9 / HBM_PEAK_GBS for k, v in kern.items()},
         "newton": {"iterations_mean": float(it[it >= 0].mean()), "wave_max_mean": float(waves.max(1).mean()),
@@ -325,6 +326,7 @@ def mix_report(w, args, dev):
         "config": {"workload": "%s: %s" % (w.key, w.title), "B": B, "C": C, "storage": w.io,
                    "passes": "fwd+bwd", "tol": w.tol, "max_iter": w.max_iter},
         "roofline": roofline(w.key, dom, d_bytes, d_ms, digest),
+        "copy_ref": copy_reference(d_bytes, d_bytes / (d_ms * 1e-3) / 1e9, dev),
         "kernels_ms": {"birkhoff_fwd_mix": fwd_ms, "birkhoff_mix_bwd": bwd_ms},
         "kernels_hbm_frac": {k: v[1] / (v[0] * 1e-3) / 1e9 / HBM_PEAK_GBS for k, v in kern.items()},
         "torch_matmul_y_ms": torch_ms,
@@ -403,6 +405,7 @@ def forward_only_report(w, args, dev):
         "config": {"workload": "%s: %s" % (w.key, w.title), "B": B, "n": n, "storage": w.io, "passes": "fwd",
                    "tol": w.tol, "max_iter": w.max_iter},
         "roofline": roofline(w.key, "birkhoff_fwd", b, ms, digest),
+        "copy_ref": copy_reference(b, b / (ms * 1e-3) / 1e9, dev),
         "newton": dict(score(st["T"]), iterations_hist=hist, iterations_mean=float(it[it >= 0].mean()),
                        wave_max_mean=float(waves.max(1).mean()), unconverged=int((it < 0).sum())),
         "sinkhorn20": dict(score(st["S"]), ms_per_launch=ms_sk, value=B / (ms_sk * 1e-3)),
@@ -552,6 +555,36 @@ def main() -> int:
     return 0
 
 
+def copy_reference(nbytes: float, achieved_gbs: float, dev, K: int = 50) -> dict:
+    """A device copy that moves the dominant kernel's algorithmic bytes per launch
+    (nbytes / 2 read, nbytes / 2 written), timed like the kernels: K back-to-back
+    copies alternating two buffer pairs, between two HIP events on the current
+    stream.  `kernel_frac` is the kernel's achieved rate over the copy's."""
+    import torch
+    half = int(nbytes) // 2
+    pairs = [(torch.empty(half, dtype=torch.uint8, device=dev), torch.empty(half, dtype=torch.uint8, device=dev))
+             for _ in range(2)]
+    for src, _ in pairs:
+        src.fill_(1)
+    stream = torch.cuda.current_stream(dev)
+    for i in range(10):
+        pairs[i % 2][1].copy_(pairs[i % 2][0])
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(K):
+        pairs[i % 2][1].copy_(pairs[i % 2][0])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    gbs = 2 * half / (ms * 1e-3) / 1e9
+    del pairs
+    torch.cuda.empty_cache()
+    return {"what": "torch copy_ of %d bytes (read + write = the kernel's bytes per launch)" % half,
+            "GBs": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS, "kernel_frac": achieved_gbs / gbs}
+
+
 def graph_replay(step, sets, K, dev):
     """ms per step when the steps are captured into a HIP graph (torch.cuda.CUDAGraph,
     50 steps per graph) and replayed: the same kernels without the host's per-launch
@@ -694,6 +727,7 @@ def forward_backward_report(w, args, dev):
         "config": {"workload": "%s: %s" % (w.key, w.title), "B": B, "n": n, "storage": w.io,
                    "passes": "fwd+bwd", "path": args.path, "tol": w.tol, "max_iter": w.max_iter},
         "roofline": roofline(w.key, dom, d_bytes, d_ms, digest),
+        "copy_ref": copy_reference(d_bytes, d_bytes / (d_ms * 1e-3) / 1e9, dev),
         "kernels_ms": {"birkhoff_fwd_bwd": fused_ms, "birkhoff_fwd": fwd_ms, "birkhoff_bwd": bwd_ms},
         "step_hbm": {"algorithmic_bytes": step_bytes,
                      "achieved_GBs": step_bytes / (ms_step * 1e-3) / 1e9,
