@@ -239,6 +239,48 @@ def test_bf16_ragged_canaries():
     check_backward(w, host_f64(dH), oracle.bwd(T_ref, W.decode_f64(Gs)))
 
 
+@pytest.mark.parametrize("B", [1, 31, 32, 33, 300, 2007])
+def test_bf16_n8_parity_and_canaries(B):
+    """bf16 storage for 8x8 matrices (lane pairs, four 16-byte chunks per lane):
+    forward, backward and the one-launch forward + backward against the oracle
+    at the bf16 gates, with sentinels around every output."""
+    print("case bf16 n8 B=%d" % B, flush=True)
+    n, pad, sent = 8, 2, 3.0
+    w = W.Workload(key="bf16n8", title="8x8 bf16, N(0,1)", B=B, n=n, io="bf16", logits=("normal", 1.0),
+                   upstream=("normal", 1.0), passes="fwd+bwd", seed=41)
+    Hs = W.make_logits(w, B=B)
+    Gs = W.make_upstream(w, B=B)
+    H = as_storage(Hs, w)
+    G = as_storage(Gs, w)
+
+    def bufs():
+        Tb = torch.full((B + 2 * pad, n, n), sent, device=DEV, dtype=torch.bfloat16)
+        Hb = torch.full((B + 2 * pad, n, n), sent, device=DEV, dtype=torch.bfloat16)
+        Db = torch.full((B + 2 * pad, n), sent, device=DEV)
+        return Tb, Hb, Db
+
+    T1b, H1b, D1b = bufs()
+    T1, dH1, d1 = T1b[pad:pad + B], H1b[pad:pad + B], D1b[pad:pad + B]
+    bp.birkhoff_fwd_bf16(H, T1, d1, w.tol, w.max_iter)
+    bp.birkhoff_bwd_bf16(H, d1, G, dH1)
+    T2b, H2b, D2b = bufs()
+    T2, dH2, d2 = T2b[pad:pad + B], H2b[pad:pad + B], D2b[pad:pad + B]
+    bp.birkhoff_fwd_bwd_bf16(H, G, T2, d2, dH2, w.tol, w.max_iter)
+    torch.cuda.synchronize()
+    for buf in (T1b, H1b, D1b, T2b, H2b, D2b):
+        assert (buf[:pad] == sent).all() and (buf[pad + B:] == sent).all()
+    # the one-launch form runs the same forward: T and the dual are bit-identical
+    assert torch.equal(T1, T2) and torch.equal(d1, d2)
+    H64 = W.decode_f64(Hs)
+    T_ref, _, st = oracle.project(H64)
+    assert (st >= 0).all()
+    dH_ref = oracle.bwd(T_ref, W.decode_f64(Gs))
+    for T, d, dH in ((T1, d1, dH1), (T2, d2, dH2)):
+        check_forward(w, H64, host_f64(T), d.cpu().numpy().astype(np.float64), T_ref)
+        assert (d[:, -1] == 0).all().item()
+        check_backward(w, host_f64(dH), dH_ref)
+
+
 def test_empty_batch_is_a_noop():
     H = torch.empty((0, 4, 4), device=DEV)
     T, dual = bp.project(H)
