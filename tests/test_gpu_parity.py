@@ -813,3 +813,39 @@ def test_parity_n8_large_logits():
     rel2, rel2_wc = conditioned_backward_check(host_f64(dH2), dH_ref, T_ref)
     print("  max updates %d, fwd err %.2e, residual %.2e, bwd rel %.2e / fused %.2e "
           "(where lambda_min > 0.1: %.2e / %.2e)" % (it.max(), err, res, rel, rel2, rel_wc, rel2_wc))
+
+
+def test_batch_beyond_32bit_offsets():
+    """2^27 + 37 matrices, so element offsets pass 2^31 and byte offsets 2^32 (the
+    largest workload stays below both): the one-launch forward + backward on
+    N(0, 1) inputs drawn on the device; every output's residual is checked on the
+    device, and a sample that includes the first and the last matrices against
+    the oracle."""
+    B, n = (1 << 27) + 37, 4
+    w = W.WORKLOADS["pr1"]
+    print("case 64-bit offsets B=%d" % B, flush=True)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(77)
+    H = torch.randn((B, n, n), generator=g, device=DEV)
+    G = torch.randn((B, n, n), generator=g, device=DEV)
+    T, dH = torch.empty_like(H), torch.empty_like(H)
+    dual = torch.empty((B, n), device=DEV)
+    bp.birkhoff_fwd_bwd(H, G, T, dual, dH, w.tol, w.max_iter)
+    torch.cuda.synchronize()
+    res, step = 0.0, 1 << 24
+    for s in range(0, B, step):
+        Td = T[s:s + step].double()
+        res = max(res, torch.maximum((Td.sum(2) - 1).abs().amax(1), (Td.sum(1) - 1).abs().amax(1)).max().item())
+        assert torch.isfinite(dH[s:s + step]).all().item()
+        assert (dual[s:s + step, -1] == 0).all().item()
+    del Td
+    assert res <= RES_TOL, res
+    idx = sample_indices(B, k=1024, seed=3)
+    it = torch.from_numpy(idx).to(DEV)
+    H64 = H[it].cpu().numpy().astype(np.float64)
+    T_ref, _, st = oracle.project(H64)
+    assert (st >= 0).all()
+    check_forward(w, H64, host_f64(T[it]), dual[it].cpu().numpy().astype(np.float64), T_ref)
+    check_backward(w, host_f64(dH[it]), oracle.bwd(T_ref, G[it].cpu().numpy().astype(np.float64)))
+    del H, G, T, dH, dual
+    torch.cuda.empty_cache()
