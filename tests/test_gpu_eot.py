@@ -266,3 +266,48 @@ def test_full_size_workload_sampled():
     assert np.abs(f64(T[it]) - T_ref).max() <= FWD_TOL
     check_backward(D[it], oracle.eot_bwd(T_ref, G[idx].astype(np.float64), a[idx].astype(np.float64),
                                          b[idx].astype(np.float64), w.eta), G[idx].astype(np.float64), T_ref, w.eta)
+
+
+def test_problems_beyond_32bit_offsets():
+    """2^26 + 29 problems of 4 x 6: the cost, plan and gradient arrays are 6.4 GB
+    each, so byte offsets pass 2^32 (the benchmark workload stays at 0.4 GB).
+    Costs and per-problem marginals (dyadic, summing to exactly one) are drawn on
+    the device; the residual of every plan is checked there in float64, and a sample
+    that includes the last problems against the oracle."""
+    B, n, m, eta = (1 << 26) + 29, 4, 6, 0.5
+    print("eot 64-bit offsets B=%d" % B, flush=True)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(93)
+    def dyadic(k):
+        # weights ~ U(0.5, 1.5) turned into multiples of 2^-20 summing to exactly one
+        wts = torch.rand((B, k), generator=g, device=DEV) + 0.5
+        q = torch.floor(wts / wts.sum(1, keepdim=True) * float(1 << 20))
+        q[torch.arange(B, device=DEV), q.argmax(1)] += float(1 << 20) - q.sum(1)
+        return q / float(1 << 20)
+
+    M = torch.randn((B, n, m), generator=g, device=DEV)
+    a, b = dyadic(n), dyadic(m)
+    assert (a.sum(1) == 1).all().item() and (b.sum(1) == 1).all().item()
+    G = torch.randn((B, n, m), generator=g, device=DEV)
+    T, dual = bp.eot_plan(M, a, b, eta)
+    D = bp.eot_plan_bwd(T, G, a, eta)
+    torch.cuda.synchronize()
+    res, step = 0.0, 1 << 23
+    for s in range(0, B, step):
+        Td = T[s:s + step].double()
+        r = torch.maximum((Td.sum(2) - a[s:s + step].double()).abs().amax(1),
+                          (Td.sum(1) - b[s:s + step].double()).abs().amax(1))
+        res = max(res, r.max().item())
+        assert torch.isfinite(D[s:s + step]).all().item()
+    del Td
+    assert res <= RES_TOL, res
+    rng = np.random.default_rng(94)
+    idx = np.unique(np.concatenate([np.arange(B - 64, B), rng.choice(B, 960, replace=False)]))
+    it = torch.from_numpy(idx).to(DEV)
+    Ms, As, Bs, Gs = f64(M[it]), f64(a[it]), f64(b[it]), f64(G[it])
+    T_ref, _, st = oracle.eot_project(Ms, As, Bs, eta)
+    assert (st >= 0).all()
+    assert np.abs(f64(T[it]) - T_ref).max() <= FWD_TOL
+    check_backward(D[it], oracle.eot_bwd(T_ref, Gs, As, Bs, eta), Gs, T_ref, eta)
+    del M, G, T, D, dual
+    torch.cuda.empty_cache()
