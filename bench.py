@@ -74,14 +74,25 @@ def roofline(workload: str, kernel: str, nbytes: float, ms: float, digest: str) 
     over the launch time, against 8 TB/s.  When committed counters exist for the
     same kernel sources, `valu_busy` adds AMD's VALUBusy measure for the same
     launch time -- SQ_ACTIVE_INST_VALU / (CUs x cycles), cycles = time x 2.4 GHz --
-    which an issue-saturated fp32 FMA loop drives to about 0.9 on this chip."""
+    which an issue-saturated fp32 FMA loop drives to about 0.9 on this chip, and
+    `valu` the launch's vector instructions (SQ_INSTS_VALU x 64 lanes) per second
+    against the fp32 issue peak of 256 CUs x 64 lanes x 2.4 GHz."""
     hbm = nbytes / (ms * 1e-3) / 1e9
     out = {"bound": "hbm", "kernel": kernel, "achieved": hbm, "peak": HBM_PEAK_GBS, "unit": "GB/s",
            "frac": hbm / HBM_PEAK_GBS, "traffic": measured_traffic(workload, kernel, digest),
            "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": ms}
-    active = _profile(workload, digest).get("valu_active_per_launch", {}).get(kernel)
+    prof = _profile(workload, digest)
+    active = prof.get("valu_active_per_launch", {}).get(kernel)
     if active is not None:
         out["valu_busy"] = active / N_CU / (ms * 1e-3 * CLOCK_HZ)
+    insts = prof.get("valu_insts_per_launch", {}).get(kernel)
+    if insts is not None:
+        # the same launch against the fp32 VALU issue peak: every CU issues one
+        # 64-lane vector instruction per cycle (the 157.3 TFLOP/s figure also counts
+        # packed two-wide FMAs, which this code does not use)
+        peak = N_CU * 64 * CLOCK_HZ
+        achieved = insts * 64 / (ms * 1e-3)
+        out["valu"] = {"achieved": achieved, "peak": peak, "unit": "lane-instructions/s", "frac": achieved / peak}
     return out
 
 

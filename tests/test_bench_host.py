@@ -38,13 +38,16 @@ def test_roofline_record(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "ROOT", tmp_path)
     (tmp_path / "profiles").mkdir()
     prof = {"kernel_digest": "abc", "bytes_per_launch": {"k": 1.5e8},
-            "valu_active_per_launch": {"k": 0.5 * 256 * 1e-4 * 2.4e9}}
+            "valu_active_per_launch": {"k": 0.5 * 256 * 1e-4 * 2.4e9},
+            "valu_insts_per_launch": {"k": 0.25 * 256 * 1e-4 * 2.4e9}}
     (tmp_path / "profiles" / "traffic_w.json").write_text(json.dumps(prof))
     r = bench.roofline("w", "k", 8e8, 0.1, "abc")      # 8e8 bytes in 0.1 ms = 8 TB/s
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
     assert abs(r["achieved"] - 8000.0) < 1e-9 and abs(r["frac"] - 1.0) < 1e-12
     assert r["traffic"] == 1.5e8
     assert abs(r["valu_busy"] - 0.5) < 1e-12
+    assert r["valu"]["unit"] == "lane-instructions/s" and abs(r["valu"]["frac"] - 0.25) < 1e-12
+    assert abs(r["valu"]["peak"] - 256 * 64 * 2.4e9) < 1.0
     # counters taken on other kernel sources are not used
     r2 = bench.roofline("w", "k", 8e8, 0.1, "other")
-    assert r2["traffic"] is None and "valu_busy" not in r2
+    assert r2["traffic"] is None and "valu_busy" not in r2 and "valu" not in r2
