@@ -96,20 +96,29 @@ def birkhoff_abi_version() -> int:
 
 # ---------------------------------------------------------------- marshalling
 
+_torch_mod = None
+
+
 def _torch():
-    import torch
-    return torch
+    global _torch_mod
+    if _torch_mod is None:
+        import torch
+        _torch_mod = torch
+    return _torch_mod
 
 
 def _stream_handle(stream, device):
-    torch = _torch()
     if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return ctypes.c_void_p(stream.cuda_stream)
+        stream = _torch().cuda.current_stream(device)
+    return stream.cuda_stream
 
 
 def _mats(x, name, dtype, B=None, n=None):
     torch = _torch()
+    if isinstance(x, torch.Tensor) and x.is_cuda and x.dtype == dtype and x.is_contiguous():
+        shp = x.shape   # the common case in one pass; the checks below name what is wrong
+        if len(shp) == 3 and shp[1] == shp[2] and (B is None or (shp[0] == B and shp[1] == n)):
+            return x
     if not isinstance(x, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
     if not x.is_cuda:
@@ -135,23 +144,29 @@ def _vec(x, name, B, n, dtype):
 
 
 def _same_device(*ts):
-    d = ts[0].device
+    i = ts[0].get_device()
     for t in ts[1:]:
-        if t.device != d:
+        if t.get_device() != i:
             raise ValueError("all tensors must be on the same device")
-    return d
+    return ts[0].device
 
 
 def _call(name, device, *args):
+    """Calls the entry point with `device` current (HIP launches on the current
+    device's view of the stream); the device switch is skipped when it already is."""
     torch = _torch()
-    with torch.cuda.device(device):
-        rc = getattr(load_library(), name)(*args)
+    fn = getattr(_lib if _lib is not None else load_library(), name)
+    if device.index == torch.cuda.current_device():
+        rc = fn(*args)
+    else:
+        with torch.cuda.device(device):
+            rc = fn(*args)
     if rc != 0:
         raise BirkhoffError(rc, name)
 
 
 def _p(t):
-    return ctypes.c_void_p(t.data_ptr())
+    return t.data_ptr()   # a plain address; the entry points' argtypes make it a void*
 
 
 # ------------------------------------------------------------- ABI wrappers
