@@ -911,3 +911,40 @@ def test_distribution_sweep(kind, n, io):
         dHg = dH_ref + np.sign(dHg - dH_ref) * np.maximum(np.abs(dHg - dH_ref) - half_ulp_bf16(dH_ref), 0.0)
     rel, rel_wc = conditioned_backward_check(dHg, dH_ref, T_ref)
     print("  bwd rel %.2e (where lambda_min > 0.1: %.2e)" % (rel, rel_wc))
+
+
+def test_binding_rejects_bad_arguments():
+    """The binding's checks, and the C ABI's behind them, reject malformed calls
+    before anything is launched; a good call still works afterwards."""
+    B = 64
+    H = torch.randn((B, 4, 4), device=DEV)
+    T = torch.empty_like(H)
+    dual = torch.empty((B, 4), device=DEV)
+    with pytest.raises(ValueError):
+        bp.birkhoff_fwd(H.cpu(), T, dual)                                  # host tensor
+    with pytest.raises(TypeError):
+        bp.birkhoff_fwd(H.double(), T, dual)                               # wrong dtype
+    with pytest.raises(ValueError):
+        bp.birkhoff_fwd(H.transpose(1, 2), T, dual)                        # not contiguous
+    with pytest.raises(ValueError):
+        bp.birkhoff_fwd(H[:, :, :3].contiguous(), T, dual)                 # not square
+    with pytest.raises(ValueError):
+        bp.birkhoff_fwd(H, torch.empty((B + 1, 4, 4), device=DEV), dual)  # T of another batch
+    with pytest.raises(ValueError):
+        bp.birkhoff_fwd(H, T, torch.empty((B, 3), device=DEV))             # dual of another shape
+    with pytest.raises(bp.BirkhoffError) as e:
+        bp.birkhoff_fwd(H, T, dual, tol=0.0)                               # tol must be positive
+    assert e.value.code == -1
+    with pytest.raises(bp.BirkhoffError) as e:
+        H5 = torch.randn((B, 5, 5), device=DEV)
+        bp.birkhoff_fwd(H5, torch.empty_like(H5), torch.empty((B, 5), device=DEV))   # n not 4 or 8
+    assert e.value.code == -1
+    base = torch.randn(B * 16 + 4, device=DEV)
+    Hmis = base[1:1 + B * 16].view(B, 4, 4)                                 # 4 bytes past a 16-byte boundary
+    assert Hmis.is_contiguous() and Hmis.data_ptr() % 16 == 4
+    with pytest.raises(bp.BirkhoffError) as e:
+        bp.birkhoff_fwd(Hmis, T, dual)
+    assert e.value.code == -2
+    bp.birkhoff_fwd(H, T, dual)
+    torch.cuda.synchronize()
+    assert residual(host_f64(T)).max() <= RES_TOL
