@@ -370,16 +370,21 @@ def test_repeatable_and_stream_ordered():
     assert torch.equal(T1, T2) and torch.equal(d1, d2) and torch.equal(dH1, dH2)
 
 
-def test_autograd_function_matches_oracle():
-    w = W.WORKLOADS["pr1"]
-    Hs = W.make_logits(w, B=512)
-    Gs = W.make_upstream(w, B=512)
-    H = dev(Hs).requires_grad_(True)
+@pytest.mark.parametrize("key", ["pr1", "n8", "bw"])
+def test_autograd_function_matches_oracle(key):
+    """torch.autograd through BirkhoffProjection: fp32 differentiates from the saved
+    T (birkhoff_bwd_from_T), bf16 storage from the saved logits and dual."""
+    w = W.WORKLOADS[key]
+    Hs = W.make_logits(w, B=512 + 7)
+    Gs = W.make_upstream(w, B=512 + 7)
+    H = as_storage(Hs, w).requires_grad_(True)
     T = bp.BirkhoffProjection.apply(H)
-    (T * dev(Gs)).sum().backward()
-    T_ref, _, _ = oracle.project(Hs.astype(np.float64))
-    assert np.abs(host_f64(T.detach()) - T_ref).max() <= FWD_TOL
-    check_backward(w, host_f64(H.grad), oracle.bwd(T_ref, Gs.astype(np.float64)))
+    (T * as_storage(Gs, w)).sum().backward()
+    H64 = W.decode_f64(Hs)
+    T_ref, _, _ = oracle.project(H64)
+    err = np.abs(host_f64(T.detach()) - T_ref)
+    assert (err <= FWD_TOL + (half_ulp_bf16(T_ref) if w.io == "bf16" else 0.0)).all(), err.max()
+    check_backward(w, host_f64(H.grad), oracle.bwd(T_ref, W.decode_f64(Gs)))
 
 
 @pytest.mark.parametrize("K", [1, 5, 20])
