@@ -698,6 +698,9 @@ def forward_backward_report(w, args, dev):
     fwd_ms = timed(run_fwd, K)           # per-kernel launch times, same stream
     bwd_ms = timed(run_bwd, K)
     fused_ms = ms_step if args.path == "fused" else ms_other
+    bwd_t_ms = None
+    if w.io == "f32":                    # the backward from T alone (what autograd uses for fp32)
+        bwd_t_ms = timed(lambda s: bp.birkhoff_bwd_from_T(s["T"], s["G"], s["dH"], stream), K)
 
     def step_on_current(s):   # the same step, launched on whatever stream is current
         if args.path == "fused":
@@ -739,7 +742,8 @@ def forward_backward_report(w, args, dev):
                    "passes": "fwd+bwd", "path": args.path, "tol": w.tol, "max_iter": w.max_iter},
         "roofline": roofline(w.key, dom, d_bytes, d_ms, digest),
         "copy_ref": copy_reference(d_bytes, d_bytes / (d_ms * 1e-3) / 1e9, dev),
-        "kernels_ms": {"birkhoff_fwd_bwd": fused_ms, "birkhoff_fwd": fwd_ms, "birkhoff_bwd": bwd_ms},
+        "kernels_ms": dict({"birkhoff_fwd_bwd": fused_ms, "birkhoff_fwd": fwd_ms, "birkhoff_bwd": bwd_ms},
+                           **({"birkhoff_bwd_from_T": bwd_t_ms} if bwd_t_ms is not None else {})),
         "step_hbm": {"algorithmic_bytes": step_bytes,
                      "achieved_GBs": step_bytes / (ms_step * 1e-3) / 1e9,
                      "frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
