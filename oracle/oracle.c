@@ -303,11 +303,26 @@ static int newton_one(const double *H, int n, double tol, int max_iter,
 
         double gn2 = 0.0;
         for (int j = 0; j < m; ++j) { g[j] = c[j] - 1.0; gn2 += g[j] * g[j]; }
+        /* h_jk = [j == k] c_j - sum_i T_ij T_ik (eq 9).  The diagonal is formed
+         * as sum_i T_ij (sum_{l != j} T_il): the same number, since every row of
+         * T sums to one (eval_T normalises it), without the cancellation of
+         * c_j - sum_i T_ij^2, which leaves no correct digit once column j is
+         * carried by one entry within 1e-16 of 1 (logit spans beyond ~40). */
         for (int j = 0; j < m; ++j)
             for (int k = 0; k < m; ++k) {
                 double p = 0.0;
-                for (int i = 0; i < n; ++i) p += T[i * n + j] * T[i * n + k];
-                hess[j * m + k] = (j == k ? c[j] : 0.0) - p;
+                if (j == k) {
+                    for (int i = 0; i < n; ++i) {
+                        double o = 0.0;
+                        for (int l = 0; l < n; ++l)
+                            if (l != j) o += T[i * n + l];
+                        p += T[i * n + j] * o;
+                    }
+                    hess[j * m + k] = p;
+                } else {
+                    for (int i = 0; i < n; ++i) p += T[i * n + j] * T[i * n + k];
+                    hess[j * m + k] = -p;
+                }
             }
         for (int j = 0; j < m; ++j) d[j] = -g[j];
         int accepted = 0;
@@ -550,11 +565,24 @@ static int eot_newton_one(const double *M, const double *a, const double *b, int
 
         double gn2 = 0.0;
         for (int j = 0; j < k1; ++j) { g[j] = c[j] - b[j]; gn2 += g[j] * g[j]; }
+        /* eta h_jk = [j == k] c_j - sum_i T_ij T_ik / a_i (eq 9); the diagonal as
+         * sum_i (T_ij / a_i) (sum_{l != j} T_il), the same number since row i of
+         * T sums to a_i, without the cancellation (see newton_one). */
         for (int j = 0; j < k1; ++j)
             for (int k = 0; k < k1; ++k) {
                 double p = 0.0;
-                for (int i = 0; i < n; ++i) p += T[i * m + j] * T[i * m + k] / a[i];
-                hess[j * k1 + k] = ((j == k ? c[j] : 0.0) - p) / eta;
+                if (j == k) {
+                    for (int i = 0; i < n; ++i) {
+                        double o = 0.0;
+                        for (int l = 0; l < m; ++l)
+                            if (l != j) o += T[i * m + l];
+                        p += T[i * m + j] / a[i] * o;
+                    }
+                    hess[j * k1 + k] = p / eta;
+                } else {
+                    for (int i = 0; i < n; ++i) p += T[i * m + j] * T[i * m + k] / a[i];
+                    hess[j * k1 + k] = -p / eta;
+                }
             }
         for (int j = 0; j < k1; ++j) d[j] = -g[j];
         int accepted = 0;

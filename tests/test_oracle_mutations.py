@@ -33,7 +33,9 @@ MUTANTS = {
     "alpha_sign": ("alpha[i] = -lse(u, n, 1);", "alpha[i] = lse(u, n, 1);"),
     "primal_beta_sign": ("exp(alpha[i] + beta[j] + H[i * n + j])", "exp(alpha[i] - beta[j] + H[i * n + j])"),
     "lost_gauge": ("beta_out[j] = beta[j] - beta[n - 1];", "beta_out[j] = beta[j];"),
-    "hessian_sign": ("hess[j * m + k] = (j == k ? c[j] : 0.0) - p;", "hess[j * m + k] = (j == k ? c[j] : 0.0) + p;"),
+    "hessian_sign": ("hess[j * m + k] = -p;", "hess[j * m + k] = p;"),
+    "hessian_diag_self": ("if (l != j) o += T[i * n + l];", "if (l != j + 1) o += T[i * n + l];"),
+    "hessian_diag_weight": ("p += T[i * n + j] * o;", "p += o;"),
     "gradient_sign": ("g[j] = c[j] - 1.0; gn2 += g[j] * g[j];", "g[j] = 1.0 - c[j]; gn2 += g[j] * g[j];"),
     "linesearch_df_sign": ("for (int j = 0; j < m; ++j) df -= gam * d[j];", "for (int j = 0; j < m; ++j) df += gam * d[j];"),
     "softmax_no_max_shift_wrong": ("double e = exp(H[i * n + j] + beta[j] - mu);", "double e = exp(H[i * n + j] - beta[j] - mu);"),
@@ -48,7 +50,9 @@ MUTANTS = {
     "eot_plan_drop_a": ("for (int j = 0; j < m; ++j) T[i * m + j] *= a[i] / s;", "for (int j = 0; j < m; ++j) T[i * m + j] *= 1.0 / s;"),
     "eot_hessian_drop_inv_a": ("for (int i = 0; i < n; ++i) p += T[i * m + j] * T[i * m + k] / a[i];",
                                "for (int i = 0; i < n; ++i) p += T[i * m + j] * T[i * m + k];"),
-    "eot_hessian_drop_eta": ("hess[j * k1 + k] = ((j == k ? c[j] : 0.0) - p) / eta;", "hess[j * k1 + k] = ((j == k ? c[j] : 0.0) - p);"),
+    "eot_hessian_diag_drop_inv_a": ("p += T[i * m + j] / a[i] * o;", "p += T[i * m + j] * o;"),
+    "eot_hessian_drop_eta": ("hess[j * k1 + k] = -p / eta;", "hess[j * k1 + k] = -p;"),
+    "eot_hessian_diag_drop_eta": ("hess[j * k1 + k] = p / eta;", "hess[j * k1 + k] = p;"),
     "eot_gradient_marginal": ("for (int j = 0; j < k1; ++j) { g[j] = c[j] - b[j]; gn2 += g[j] * g[j]; }",
                               "for (int j = 0; j < k1; ++j) { g[j] = c[j] - 1.0 / m; gn2 += g[j] * g[j]; }"),
     "eot_df_drop_eta": ("df += eta * a[i] * log1p(acc);", "df += a[i] * log1p(acc);"),
