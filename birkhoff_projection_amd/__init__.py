@@ -59,7 +59,7 @@ def load_library():
     vp, i64, ci, cf = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
     sig = {
         "birkhoff_fwd": [vp, vp, vp, i64, ci, cf, ci, vp],
-        "birkhoff_fwd_ex": [vp, vp, vp, vp, i64, ci, cf, ci, vp],
+        "birkhoff_fwd_ex": [vp, vp, vp, vp, vp, i64, ci, cf, ci, vp],
         "birkhoff_bwd": [vp, vp, vp, vp, i64, ci, vp],
         "birkhoff_bwd_from_T": [vp, vp, vp, i64, ci, vp],
         "sinkhorn_fwd": [vp, vp, i64, ci, ci, vp],
@@ -183,16 +183,23 @@ def birkhoff_fwd(logits, T, dual, tol: float = 1e-6, max_iter: int = 50, stream=
           _stream_handle(stream, dev))
 
 
-def birkhoff_fwd_ex(logits, T, dual, iters, tol: float = 1e-6, max_iter: int = 50, stream=None) -> None:
-    """As birkhoff_fwd, also writing iters [B] int32 (updates used, -1 if tol not reached)."""
+def birkhoff_fwd_ex(logits, T, dual, iters, tol: float = 1e-6, max_iter: int = 50, stream=None,
+                    fallbacks=None) -> None:
+    """As birkhoff_fwd, also writing iters [B] int32 (updates used, -1 if tol not reached)
+    and, if given, fallbacks [B] int32 (how many of the updates were fallback sweeps)."""
     torch = _torch()
     _mats(logits, "logits", torch.float32)
     B, n = logits.shape[0], logits.shape[1]
     _mats(T, "T", torch.float32, B, n)
     _vec(dual, "dual", B, n, torch.float32)
     _vec(iters, "iters", B, None, torch.int32)
-    dev = _same_device(logits, T, dual, iters)
-    _call("birkhoff_fwd_ex", dev, _p(logits), _p(T), _p(dual), _p(iters), B, n, float(tol), int(max_iter),
+    if fallbacks is not None:
+        _vec(fallbacks, "fallbacks", B, None, torch.int32)
+        dev = _same_device(logits, T, dual, iters, fallbacks)
+    else:
+        dev = _same_device(logits, T, dual, iters)
+    _call("birkhoff_fwd_ex", dev, _p(logits), _p(T), _p(dual), _p(iters),
+          None if fallbacks is None else _p(fallbacks), B, n, float(tol), int(max_iter),
           _stream_handle(stream, dev))
 
 
@@ -510,7 +517,9 @@ def _autograd_function():
     class BirkhoffProjection(torch.autograd.Function):
         """T = proj_KL(exp(logits)) onto B_n with the implicit (eq 13) backward.
 
-        No Newton iterates are kept.  fp32 saves the output T and differentiates
+        No Newton iterates are kept.  The backward is computed by the kernels (not
+        from differentiable torch operations), so it is once differentiable: a
+        second derivative through it raises.  fp32 saves the output T and differentiates
         from it (birkhoff_bwd_from_T: the pages' backward from T* and G, 192 bytes
         per 4x4 projection and no exponentials, 6 % faster than recomputing T);
         bf16 storage saves (logits, dual) and recomputes T in fp32, since a
@@ -528,6 +537,7 @@ def _autograd_function():
             return T
 
         @staticmethod
+        @torch.autograd.function.once_differentiable
         def backward(ctx, dT):
             saved = ctx.saved_tensors
             dT = dT.contiguous()
@@ -551,6 +561,7 @@ def _autograd_function():
             return T
 
         @staticmethod
+        @torch.autograd.function.once_differentiable
         def backward(ctx, dT):
             T, a = ctx.saved_tensors
             return eot_plan_bwd(T, dT.contiguous(), a, ctx.eta), None, None, None, None, None
@@ -566,6 +577,7 @@ def _autograd_function():
             return y
 
         @staticmethod
+        @torch.autograd.function.once_differentiable
         def backward(ctx, dy):
             T, x = ctx.saved_tensors
             dH, dx = project_mix_bwd(T, x.contiguous(), dy.contiguous())

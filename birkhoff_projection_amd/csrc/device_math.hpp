@@ -134,6 +134,16 @@ __device__ __forceinline__ void stream_store(uint4* p, const uint4& v) {
     __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
 }
 
+// A copy of v that the compiler cannot see through (an empty asm statement that
+// claims to modify the register; no instruction is emitted): addresses derived
+// from it are recomputed where they are used, a few instructions, instead of
+// being kept live -- or spilled -- across a long iteration between the load
+// and the store of a tile.
+__device__ __forceinline__ int opaque(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
 // ---- movement of one matrix per lane between HBM and registers ------------
 //
 // A wave owns 64 consecutive matrices, one per lane, each C 16-byte chunks long
@@ -241,6 +251,7 @@ struct WaveTile {
 
     // Waits for a prefetch and hands each lane its own C chunks.
     __device__ __forceinline__ static void read_prefetched(uint4* lds, int lane, uint4 (&own)[C]) {
+        lane = opaque(lane);
         __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0): the LDS copies have landed
         wave_lds_sync();
 #pragma unroll
@@ -253,6 +264,7 @@ struct WaveTile {
     __device__ __forceinline__ static void store_except(const uint4 (&own)[C], uint4* lds, int lane,
                                                         uint4* __restrict__ dst, int valid, uint64_t skip) {
         static_assert(kStaged, "staged tiles only");
+        lane = opaque(lane);
 #pragma unroll
         for (int q = 0; q < C; ++q) lds[slot(lane, q)] = own[q];
         wave_lds_sync();
@@ -269,6 +281,7 @@ struct WaveTile {
     // exist; the rest are not written.  A full tile stores unconditionally.
     __device__ __forceinline__ static void store(const uint4 (&own)[C], uint4* lds, int lane, uint4* __restrict__ dst,
                                                  int valid) {
+        lane = opaque(lane);
         const bool full = valid == 64 * C;
         if constexpr (kStaged) {
 #pragma unroll

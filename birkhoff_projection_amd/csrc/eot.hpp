@@ -445,57 +445,85 @@ eot_fwd_kernel(const float* __restrict__ cost, const float* __restrict__ a_in, c
     col_sums<N, M>(S, a, c);
     float res = ln.valid() ? col_residual<M>(c, b) : 0.0f;
     int it = 0;
+    // Lanes with lost entries, as in the Birkhoff iteration (birk::newton_iterate):
+    // S is formed multiplicatively, so an entry that underflowed stays zero.  A
+    // lane is `wide` when S has an entry below kTiny at the start (cost spans of
+    // about 70 eta), or when it converges with one and S rebuilt from the costs at
+    // its dual misses tol; a wide lane re-evaluates S from the costs after every
+    // accepted step.
+    float smin = S[0];
+#pragma unroll
+    for (int k = 1; k < N * M; ++k) smin = fminf(smin, S[k]);
+    bool wide = ln.valid() && smin < kTiny;
 
-    while (res > tol && it < max_iter) {
-        float g[K1], rhs[K1], d[K1];
+    for (;;) {
+        while (res > tol && it < max_iter) {
+            float g[K1], rhs[K1], d[K1];
 #pragma unroll
-        for (int j = 0; j < K1; ++j) {
-            g[j] = c[j] - b[j];
-            rhs[j] = -g[j];
-        }
-        float gn2 = g[0] * g[0];
+            for (int j = 0; j < K1; ++j) {
+                g[j] = c[j] - b[j];
+                rhs[j] = -g[j];
+            }
+            float gn2 = g[0] * g[0];
 #pragma unroll
-        for (int j = 1; j < K1; ++j) gn2 = fmaf(g[j], g[j], gn2);
-        float h[Tri<M>::S];
-        hessian<N, M>(S, a, h);
-        damp<M>(h);
-        const bool ok = SpdSolve<M>::run(h, rhs, d);
+            for (int j = 1; j < K1; ++j) gn2 = fmaf(g[j], g[j], gn2);
+            float h[Tri<M>::S];
+            hessian<N, M>(S, a, h);
+            damp<M>(h);
+            const bool ok = SpdSolve<M>::run(h, rhs, d);
 
-        bool accepted = false;
-        if (ok) {
-            for (int k = 0; k < 5; ++k) {
-                const float gam = step_size(k);
-                float s[K1], e[K1], rr[N], ct[M];
+            bool accepted = false;
+            if (ok) {
+                for (int k = 0; k < 5; ++k) {
+                    const float gam = step_size(k);
+                    float s[K1], e[K1], rr[N], ct[M];
 #pragma unroll
-                for (int j = 0; j < K1; ++j) s[j] = gam * d[j];
-                float noise;
-                const float df = trial_point<N, M>(S, a, c, g, s, e, rr, ct, noise);
-                float gt2 = (ct[0] - b[0]) * (ct[0] - b[0]);
+                    for (int j = 0; j < K1; ++j) s[j] = gam * d[j];
+                    float noise;
+                    const float df = trial_point<N, M>(S, a, c, g, s, e, rr, ct, noise);
+                    float gt2 = (ct[0] - b[0]) * (ct[0] - b[0]);
 #pragma unroll
-                for (int j = 1; j < K1; ++j) gt2 = fmaf(ct[j] - b[j], ct[j] - b[j], gt2);
-                if (df < noise && gt2 < gn2) {
+                    for (int j = 1; j < K1; ++j) gt2 = fmaf(ct[j] - b[j], ct[j] - b[j], gt2);
+                    if (df < noise && gt2 < gn2) {
 #pragma unroll
-                    for (int j = 0; j < K1; ++j) y[j] = fmaf(s[j], kLog2e, y[j]);
-                    accept_trial<N, M>(S, e, rr);
+                        for (int j = 0; j < K1; ++j) y[j] = fmaf(s[j], kLog2e, y[j]);
+                        accept_trial<N, M>(S, e, rr);
 #pragma unroll
-                    for (int j = 0; j < M; ++j) c[j] = ct[j];
-                    accepted = true;
-                    break;
+                        for (int j = 0; j < M; ++j) c[j] = ct[j];
+                        accepted = true;
+                        break;
+                    }
                 }
             }
-        }
-        if (!accepted) {
-            // the logits are re-read (by this lane alone) only on this rare path
-            float L[N * M];
-            const float* p = cost + ln.problem() * (N * M);
+            if (!accepted || wide) {
+                // the fallback sweep, or a wide lane's step: S from the costs (re-read
+                // by this lane alone, only on these rare paths)
+                float L[N * M];
+                const float* p = cost + ln.problem() * (N * M);
 #pragma unroll
-            for (int k = 0; k < N * M; ++k) L[k] = p[k] * lscale;
-            sinkhorn_sweep<N, M>(L, a, b, y);
-            softmax_rows<M, N>(L, y, S);
-            col_sums<N, M>(S, a, c);
+                for (int k = 0; k < N * M; ++k) L[k] = p[k] * lscale;
+                if (!accepted) sinkhorn_sweep<N, M>(L, a, b, y);
+                softmax_rows<M, N>(L, y, S);
+                col_sums<N, M>(S, a, c);
+            }
+            ++it;
+            res = col_residual<M>(c, b);
         }
-        ++it;
+        if (!(res <= tol) || wide) break;
+        float mn = S[0];
+#pragma unroll
+        for (int k = 1; k < N * M; ++k) mn = fminf(mn, S[k]);
+        if (mn >= kTiny) break;
+        // converged with an entry below kTiny: checked against its dual once
+        wide = true;
+        float L[N * M];
+        const float* p = cost + ln.problem() * (N * M);
+#pragma unroll
+        for (int k = 0; k < N * M; ++k) L[k] = p[k] * lscale;
+        softmax_rows<M, N>(L, y, S);
+        col_sums<N, M>(S, a, c);
         res = col_residual<M>(c, b);
+        if (res <= tol) break;
     }
 
     {
@@ -565,9 +593,11 @@ eot_bwd_kernel(const float* __restrict__ Tin, const float* __restrict__ Gin, con
         for (int i = 1; i < N; ++i) s = fmaf(T[i * M + j], G[i * M + j] - nu[i], s);
         rhs[j] = s;
     }
-    float h[Tri<M>::S], w[K1];
-    hessian<N, M>(S, a, h);
-    SpdSolve<M>::run(h, rhs, w);
+    float w[K1];
+    float mass = a[0];   // bounds the entries of the Hessian
+#pragma unroll
+    for (int i = 1; i < N; ++i) mass += a[i];
+    solve_delta<M>([&](float (&h)[Tri<M>::S]) { hessian<N, M>(S, a, h); }, rhs, w, mass);
     const float ieta = 1.0f / eta;
     float D[N * M];
 #pragma unroll

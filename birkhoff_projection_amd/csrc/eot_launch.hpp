@@ -8,6 +8,7 @@
 #include <cstdint>
 
 #include "eot.hpp"
+#include "launch.hpp"
 
 namespace birk {
 namespace eot {
@@ -39,40 +40,40 @@ struct BwdArgs {
 };
 
 template <int N, int M>
-void launch(const FwdArgs& x) {
+int launch_shape(const FwdArgs& x) {
     const dim3 g = grid_for<N, M>(x.B), blk(Waves<N * M>::threads);
     if (x.iters)
-        hipLaunchKernelGGL((birk::eot::eot_fwd_kernel<N, M, true>), g, blk, 0, x.s, x.cost, x.a, x.b, x.shared, x.T,
-                           x.dual, x.iters, x.B, x.eta, x.tol, x.max_iter);
-    else
-        hipLaunchKernelGGL((birk::eot::eot_fwd_kernel<N, M, false>), g, blk, 0, x.s, x.cost, x.a, x.b, x.shared, x.T,
-                           x.dual, x.iters, x.B, x.eta, x.tol, x.max_iter);
+        return birk::launch(eot_fwd_kernel<N, M, true>, g, blk, x.s, x.cost, x.a, x.b, x.shared, x.T, x.dual,
+                            x.iters, x.B, x.eta, x.tol, x.max_iter);
+    return birk::launch(eot_fwd_kernel<N, M, false>, g, blk, x.s, x.cost, x.a, x.b, x.shared, x.T, x.dual, x.iters,
+                        x.B, x.eta, x.tol, x.max_iter);
 }
 
 template <int N, int M>
-void launch(const BwdArgs& x) {
+int launch_shape(const BwdArgs& x) {
     const dim3 g = grid_for<N, M>(x.B), blk(Waves<N * M>::threads);
-    hipLaunchKernelGGL((birk::eot::eot_bwd_kernel<N, M>), g, blk, 0, x.s, x.T, x.G, x.a, x.shared, x.D, x.B, x.eta);
+    return birk::launch(eot_bwd_kernel<N, M>, g, blk, x.s, x.T, x.G, x.a, x.shared, x.D, x.B, x.eta);
 }
 
-// launches the kernel for n = N rows and m columns, m in [2, 8]
+// launches the kernel for n = N rows and m columns, m in [2, 8]; returns
+// BIRKHOFF_OK or BIRKHOFF_ELAUNCH
 template <int N, typename Args>
-void by_m(int m, const Args& x) {
+int by_m(int m, const Args& x) {
     switch (m) {
-        case 2: launch<N, 2>(x); break;
-        case 3: launch<N, 3>(x); break;
-        case 4: launch<N, 4>(x); break;
-        case 5: launch<N, 5>(x); break;
-        case 6: launch<N, 6>(x); break;
-        case 7: launch<N, 7>(x); break;
-        default: launch<N, 8>(x); break;
+        case 2: return launch_shape<N, 2>(x);
+        case 3: return launch_shape<N, 3>(x);
+        case 4: return launch_shape<N, 4>(x);
+        case 5: return launch_shape<N, 5>(x);
+        case 6: return launch_shape<N, 6>(x);
+        case 7: return launch_shape<N, 7>(x);
+        default: return launch_shape<N, 8>(x);
     }
 }
 
 // each instantiated in one of the eot_rows_*.hip units
 #define BIRK_EOT_ROWS(N)                                   \
-    extern template void by_m<N, FwdArgs>(int, const FwdArgs&); \
-    extern template void by_m<N, BwdArgs>(int, const BwdArgs&);
+    extern template int by_m<N, FwdArgs>(int, const FwdArgs&); \
+    extern template int by_m<N, BwdArgs>(int, const BwdArgs&);
 BIRK_EOT_ROWS(1)
 BIRK_EOT_ROWS(2)
 BIRK_EOT_ROWS(3)

@@ -4,11 +4,11 @@
 
 namespace birk {
 namespace eot {
-template void by_m<1, FwdArgs>(int, const FwdArgs&);
-template void by_m<1, BwdArgs>(int, const BwdArgs&);
-template void by_m<2, FwdArgs>(int, const FwdArgs&);
-template void by_m<2, BwdArgs>(int, const BwdArgs&);
-template void by_m<3, FwdArgs>(int, const FwdArgs&);
-template void by_m<3, BwdArgs>(int, const BwdArgs&);
+template int by_m<1, FwdArgs>(int, const FwdArgs&);
+template int by_m<1, BwdArgs>(int, const BwdArgs&);
+template int by_m<2, FwdArgs>(int, const FwdArgs&);
+template int by_m<2, BwdArgs>(int, const BwdArgs&);
+template int by_m<3, FwdArgs>(int, const FwdArgs&);
+template int by_m<3, BwdArgs>(int, const BwdArgs&);
 }  // namespace eot
 }  // namespace birk

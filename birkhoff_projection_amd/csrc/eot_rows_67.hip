@@ -4,9 +4,9 @@
 
 namespace birk {
 namespace eot {
-template void by_m<6, FwdArgs>(int, const FwdArgs&);
-template void by_m<6, BwdArgs>(int, const BwdArgs&);
-template void by_m<7, FwdArgs>(int, const FwdArgs&);
-template void by_m<7, BwdArgs>(int, const BwdArgs&);
+template int by_m<6, FwdArgs>(int, const FwdArgs&);
+template int by_m<6, BwdArgs>(int, const BwdArgs&);
+template int by_m<7, FwdArgs>(int, const FwdArgs&);
+template int by_m<7, BwdArgs>(int, const BwdArgs&);
 }  // namespace eot
 }  // namespace birk

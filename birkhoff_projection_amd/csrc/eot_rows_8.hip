@@ -4,7 +4,7 @@
 
 namespace birk {
 namespace eot {
-template void by_m<8, FwdArgs>(int, const FwdArgs&);
-template void by_m<8, BwdArgs>(int, const BwdArgs&);
+template int by_m<8, FwdArgs>(int, const FwdArgs&);
+template int by_m<8, BwdArgs>(int, const BwdArgs&);
 }  // namespace eot
 }  // namespace birk

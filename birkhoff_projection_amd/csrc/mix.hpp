@@ -174,7 +174,8 @@ project_mix_kernel(const float* __restrict__ logits, const XT* __restrict__ x, f
     if (wave == 0) {
         const Gm geo(B, first, kTokens);
         float T[16], yv[3], res;
-        newton_solve<4, float>(geo, tile, logits, tol, max_iter, T, yv, res);
+        int sweeps;
+        newton_solve<4, float>(geo, tile, logits, tol, max_iter, T, yv, res, sweeps);
         store_forward<4, float>(geo, tile, Tout, dual, T, yv);
         if (lane < kTokens)
 #pragma unroll

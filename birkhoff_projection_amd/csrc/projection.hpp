@@ -52,6 +52,7 @@ template <>
 struct Pair<1> {
     __device__ __forceinline__ static float sum(float v) { return v; }
     __device__ __forceinline__ static float max(float v) { return v; }
+    __device__ __forceinline__ static float min(float v) { return v; }
     __device__ __forceinline__ static float prod_m1(float q) { return q; }
 };
 
@@ -66,6 +67,7 @@ struct Pair<2> {
     }
     __device__ __forceinline__ static float sum(float v) { return v + other(v); }
     __device__ __forceinline__ static float max(float v) { return fmaxf(v, other(v)); }
+    __device__ __forceinline__ static float min(float v) { return fminf(v, other(v)); }
     // (1 + q)(1 + q') - 1 for the two halves' partial products
     __device__ __forceinline__ static float prod_m1(float q) {
         const float o = other(q);
@@ -158,6 +160,24 @@ __device__ __forceinline__ float col_residual(const float (&c)[N]) {
     return r;
 }
 
+// Entries of T below this are taken as possibly inexact.  The iteration moves T
+// multiplicatively (trial points scale the columns of the current T), so an
+// entry that has underflowed to zero, or lost bits as a subnormal, stays so; a
+// T with an entry this small is therefore checked against its dual before it
+// is accepted (newton_iterate).  2^-100 leaves 26 binades above the smallest
+// normal number, and no entry this small can move a column sum by 1e-30.
+constexpr float kTiny = 0x1.0p-100f;
+
+// smallest entry of the matrix (over the R lanes that hold it); ordinary
+// minimum: the callers only use it for matrices whose residual is finite
+template <int N>
+__device__ __forceinline__ float min_entry(const float (&T)[Split<N>::K * N]) {
+    float m = T[0];
+#pragma unroll
+    for (int k = 1; k < Split<N>::K * N; ++k) m = fminf(m, T[k]);
+    return Pair<Split<N>::R>::min(m);
+}
+
 // Hessian of the reduced dual objective, eq (9) with eta = 1, a = b = 1:
 //   h_jk = [j == k] c_j - sum_i T_ij T_ik,   j, k < N-1.
 // With the column Gram sums G_jk = sum_i T_ij T_ik (all N columns), the
@@ -217,18 +237,21 @@ __device__ __forceinline__ void damp(float (&h)[Tri<N>::S]) {
     for (int j = 0; j < N - 1; ++j) h[Tri<N>::at(j, j)] += delta;
 }
 
-// x = H^{-1} r for the symmetric positive definite (N-1) x (N-1) matrix H.
-// N = 4: the closed-form adjugate of eq (12).  Other N: Cholesky H = L L^T in
-// registers.  Returns false when H is not numerically positive definite (a
-// non-positive or non-finite determinant / pivot); x is then meaningless.  The
-// Hessians solved here have bounded entries (at most n for the Birkhoff
-// kernels, whose T lies in [0, 1]; at most the total of the marginals a in the
-// general problem), so for finite inputs a pivot or the determinant is finite
-// or NaN, and one comparison with the smallest normal number (false for NaN)
-// decides.
+// x = H^{-1} r for the symmetric positive definite (N-1) x (N-1) matrix H by a
+// Cholesky factorisation H = L L^T in registers (backward stable: the computed
+// x solves a system within a few ulps of H, however ill-conditioned).  Returns
+// false when H is not numerically positive definite (a non-positive or
+// non-finite pivot); x is then meaningless.  The Hessians solved here have
+// bounded entries (at most n for the Birkhoff kernels, whose T lies in [0, 1];
+// at most the total of the marginals a in the general problem), so for finite
+// inputs a pivot is finite or NaN, and one comparison with the smallest
+// normal number (false for NaN) decides.
 template <int N>
-struct SpdSolve {
-    __device__ __forceinline__ static bool run(const float (&h)[Tri<N>::S], const float (&r)[N - 1], float (&x)[N - 1]) {
+struct CholSolve {
+    // min_pivot: pivots at or below it count as failure (default: the smallest
+    // normal number)
+    __device__ __forceinline__ static bool run(const float (&h)[Tri<N>::S], const float (&r)[N - 1], float (&x)[N - 1],
+                                               float min_pivot = 1.17549435e-38f) {
         constexpr int M = N - 1;
         float l[Tri<N>::S];   // Cholesky factor, packed lower triangle
         float dinv[M];        // 1 / l_jj
@@ -238,7 +261,7 @@ struct SpdSolve {
             float s = h[Tri<N>::at(j, j)];
 #pragma unroll
             for (int k = 0; k < j; ++k) s = fmaf(-l[Tri<N>::at(j, k)], l[Tri<N>::at(j, k)], s);
-            ok = ok && (s > 1.17549435e-38f);
+            ok = ok && (s > min_pivot);
             const float ri = rsq(s);
             dinv[j] = ri;
             l[Tri<N>::at(j, j)] = s * ri;
@@ -269,6 +292,12 @@ struct SpdSolve {
     }
 };
 
+// The Newton system of the forward: N = 4 uses the closed-form adjugate of
+// eq (12), other N the Cholesky solve.  Same contract as CholSolve (false when
+// the determinant is not a positive normal number).
+template <int N>
+struct SpdSolve : CholSolve<N> {};
+
 template <>
 struct SpdSolve<4> {
     // eq (12): cofactors of the symmetric 3x3 H, det(H) by the first column,
@@ -289,6 +318,57 @@ struct SpdSolve<4> {
         return det > 1.17549435e-38f;
     }
 };
+
+// Solves Delta w = rhs for eq (13)'s w_{-n}, Delta being the Hessian at the
+// projection (entries at most `unit` in magnitude: 1 here, the total mass of
+// the marginals in the general problem), formed by `fill(h)` as a packed lower
+// triangle.  Near a permutation Delta is numerically singular: its entries
+// that involve rows and columns carried by one entry near 1 are tiny or zero.
+// The system stays consistent there (rhs vanishes along the same directions,
+// up to its rounding, a few ulps of |G o T|), and dH = (G - v 1^T - 1 w^T) o T
+// does not depend on the component of w along them -- at an exact permutation
+// Delta = 0, rhs = 0 and dH = 0 for every w -- but the plain solution puts
+// rhs's rounding / lambda into that component, and a w that large leaves its
+// own rounding in dH.  So:
+//   - first Delta is factored as it is, and a Cholesky pivot at or below
+//     2^-24 unit (one ulp of the entry bound) counts as failure.  The pivots
+//     are at least lambda_min(Delta), so every Delta that fp32 resolves is
+//     solved exactly as eq (13) says, and its w carries at most a few |G o T|
+//     of rounding;
+//   - otherwise the solve is repeated with 2^-20 (unit + tr Delta) added to
+//     the diagonal (16 ulps of the entry bound and of the trace), which keeps
+//     what rounding can put into w within |G o T| and covers the rounding of
+//     Delta's diagonal (at most n - 2 ulps of the trace: Delta is a grounded
+//     Laplacian of the column Gram sums, diagonally dominant up to that), so
+//     that its pivots stay above 2^-25 unit.  fill is called again for it, so
+//     that h need not stay live through the first factorisation;
+//   - it fails then only when Delta is not finite (a non-finite T): w = 0, and
+//     the NaN stays in dH.
+// The solve is the Cholesky one for every n: eq (13) needs Delta^{-1} rhs, not
+// eq (12)'s closed form, and Cramer's rule (the adjugate) is not backward
+// stable -- on a nearly singular 3 x 3 Delta its solution misses the system by
+// a fraction of rhs.
+template <int N, typename Fill>
+__device__ __forceinline__ void solve_delta(Fill fill, const float (&rhs)[N - 1], float (&w)[N - 1],
+                                            float unit = 1.0f) {
+    float shift = 0.0f, min_pivot = unit * 0x1.0p-24f;   // the first attempt: Delta as it is
+#pragma unroll 1
+    for (int attempt = 0; attempt < 2; ++attempt) {
+        float h[Tri<N>::S];
+        fill(h);
+        float tr = h[Tri<N>::at(0, 0)];
+#pragma unroll
+        for (int j = 1; j < N - 1; ++j) tr += h[Tri<N>::at(j, j)];
+        const float delta = (unit + tr) * shift;
+#pragma unroll
+        for (int j = 0; j < N - 1; ++j) h[Tri<N>::at(j, j)] += delta;
+        if (CholSolve<N>::run(h, rhs, w, min_pivot)) return;
+        shift = 0x1.0p-20f;
+        min_pivot = unit * 0x1.0p-25f;
+    }
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j) w[j] = 0.0f;
+}
 
 // Trial point x + s of the line search (natural units, s_{N-1} = 0), evaluated
 // from the current T instead of from the logits.  Rows of T are softmaxes of
@@ -497,6 +577,20 @@ __device__ __forceinline__ void load_dual(const float* __restrict__ dual, int64_
     }
 }
 
+// Where a lane's item index comes from, for the rare paths that re-read its
+// logits.  WaveItem: the wave's first item (wave-uniform, in scalar registers)
+// plus the lane's id, recomputed where it is needed instead of held in vector
+// registers through the iteration.  LaneItem: an arbitrary item per lane (the
+// gathered stragglers).
+struct WaveItem {
+    int64_t base;
+    __device__ __forceinline__ int64_t get() const { return base + (int64_t)__lane_id(); }
+};
+struct LaneItem {
+    int64_t item;
+    __device__ __forceinline__ int64_t get() const { return item; }
+};
+
 // One lane reads its own item directly (used off the main path, where the
 // other lanes of the wave do not take part).
 template <int N, typename IO>
@@ -517,62 +611,95 @@ __device__ __forceinline__ void load_own(const IO* __restrict__ p, int64_t item,
 // Newton's method on the reduced dual (eq 8) from the lane's current iterate
 // (T, y, its column sums c and residual res, it updates so far) until the
 // column-sum residual is <= tol or it reaches max_iter.  `item` is the lane's
-// item index, whose logits the rare fallback sweep re-reads.
-template <int N, typename IO>
-__device__ __forceinline__ void newton_iterate(const IO* __restrict__ logits, int64_t item, float tol, int max_iter,
+// item index, whose logits the rare fallback sweep re-reads; `sweeps` counts
+// the fallback sweeps taken.
+//
+// Checked convergence.  Rows of T are Softmax(H_i. + beta) ([P] section 3.1),
+// and the projection is the unique doubly stochastic matrix of that form ([P]
+// section 2.2, eq 1).  The iteration forms T multiplicatively (a trial point
+// scales the columns of the current T), which keeps every entry's relative
+// accuracy except for entries that underflow: logit spans beyond about 100
+// give row softmaxes with entries below 2^-149, which stay zero, and subnormal
+// ones keep a few bits, so the iteration could converge to the projection of a
+// different matrix.  A lane that converges with an entry below kTiny, or that
+// started with one (`wide`, set by newton_start), therefore rebuilds T from
+// the logits at its dual once (`checked`) and goes on iterating from it:
+// entries lost on the way are back, and since the rebuilt T is exactly of the
+// form above at the fp32 dual, one or two more updates bring its column sums
+// (off by the dual's accumulated rounding) back within tol, or, with lost mass,
+// the iteration continues until they are.  Updates are counted as before; a
+// lane whose check falls on its last allowed update ends with count -1 if the
+// rebuilt T misses tol.  Lanes whose entries all stay above kTiny -- every
+// benchmark input -- take none of this.
+template <int N, typename IO, typename Item>
+__device__ __forceinline__ void newton_iterate(const IO* __restrict__ logits, Item item, float tol, int max_iter,
                                                float (&T)[Split<N>::K * N], float (&y)[N - 1], float (&c)[N],
-                                               float& res, int& it) {
+                                               float& res, int& it, bool& wide, bool& checked, int& sweeps) {
     constexpr int M = N - 1, K = Split<N>::K;
-    while (res > tol && it < max_iter) {
-        float g[M], r[M], d[M];
+    for (;;) {
+        while (res > tol && it < max_iter) {
+            float g[M], r[M], d[M];
 #pragma unroll
-        for (int j = 0; j < M; ++j) {
-            g[j] = c[j] - 1.0f;
-            r[j] = -g[j];
-        }
-        float gn2 = g[0] * g[0];
+            for (int j = 0; j < M; ++j) {
+                g[j] = c[j] - 1.0f;
+                r[j] = -g[j];
+            }
+            float gn2 = g[0] * g[0];
 #pragma unroll
-        for (int j = 1; j < M; ++j) gn2 = fmaf(g[j], g[j], gn2);
-        float h[Tri<N>::S];
-        hessian<N>(T, h);
-        damp<N>(h);
-        const bool ok = SpdSolve<N>::run(h, r, d);   // d = -H^{-1} g
+            for (int j = 1; j < M; ++j) gn2 = fmaf(g[j], g[j], gn2);
+            float h[Tri<N>::S];
+            hessian<N>(T, h);
+            damp<N>(h);
+            const bool ok = SpdSolve<N>::run(h, r, d);   // d = -H^{-1} g
 
-        bool accepted = false;
-        if (ok) {
-            for (int k = 0; k < 5; ++k) {
-                const float gam = step_size(k);
-                float s[M], e[M], rr[K], ct[N];
+            bool accepted = false;
+            if (ok) {
+                for (int k = 0; k < 5; ++k) {
+                    const float gam = step_size(k);
+                    float s[M], e[M], rr[K], ct[N];
 #pragma unroll
-                for (int j = 0; j < M; ++j) s[j] = gam * d[j];
-                float noise;
-                const float df = trial_point<N>(T, s, e, rr, ct, noise);
-                float gt2 = (ct[0] - 1.0f) * (ct[0] - 1.0f);
+                    for (int j = 0; j < M; ++j) s[j] = gam * d[j];
+                    float noise;
+                    const float df = trial_point<N>(T, s, e, rr, ct, noise);
+                    float gt2 = (ct[0] - 1.0f) * (ct[0] - 1.0f);
 #pragma unroll
-                for (int j = 1; j < M; ++j) gt2 = fmaf(ct[j] - 1.0f, ct[j] - 1.0f, gt2);
-                // the objective must not increase beyond what fp32 can resolve, and
-                // the gradient norm must decrease
-                if (df < noise && gt2 < gn2) {
+                    for (int j = 1; j < M; ++j) gt2 = fmaf(ct[j] - 1.0f, ct[j] - 1.0f, gt2);
+                    // the objective must not increase beyond what fp32 can resolve, and
+                    // the gradient norm must decrease
+                    if (df < noise && gt2 < gn2) {
 #pragma unroll
-                    for (int j = 0; j < M; ++j) y[j] = fmaf(s[j], kLog2e, y[j]);
-                    accept_trial<N>(T, e, rr);
+                        for (int j = 0; j < M; ++j) y[j] = fmaf(s[j], kLog2e, y[j]);
+                        accept_trial<N>(T, e, rr);
 #pragma unroll
-                    for (int j = 0; j < N; ++j) c[j] = ct[j];
-                    accepted = true;
-                    break;
+                        for (int j = 0; j < N; ++j) c[j] = ct[j];
+                        accepted = true;
+                        break;
+                    }
                 }
             }
-        }
-        if (!accepted) {
-            float L[K * N];
-            load_own<N, IO>(logits, item, L);
+            if (!accepted) {
+                float L[K * N];
+                load_own<N, IO>(logits, item.get(), L);
 #pragma unroll
-            for (int k = 0; k < K * N; ++k) L[k] *= kLog2e;
-            sinkhorn_sweep<N>(L, y);
-            softmax_rows<N, K>(L, y, T);
-            col_sums<N>(T, c);
+                for (int k = 0; k < K * N; ++k) L[k] *= kLog2e;
+                sinkhorn_sweep<N>(L, y);
+                softmax_rows<N, K>(L, y, T);
+                col_sums<N>(T, c);
+                ++sweeps;
+            }
+            ++it;
+            res = col_residual<N>(c);
         }
-        ++it;
+        // converged (or out of updates, or not finite): a suspect lane is rebuilt once
+        if (!(res <= tol) || checked || (!wide && min_entry<N>(T) >= kTiny)) break;
+        checked = true;
+        wide = false;
+        float L[K * N];
+        load_own<N, IO>(logits, item.get(), L);
+#pragma unroll
+        for (int k = 0; k < K * N; ++k) L[k] *= kLog2e;
+        softmax_rows<N, K>(L, y, T);
+        col_sums<N>(T, c);
         res = col_residual<N>(c);
     }
 }
@@ -580,13 +707,16 @@ __device__ __forceinline__ void newton_iterate(const IO* __restrict__ logits, in
 // Loads the wave's logits and evaluates the start x^(0) (kStartSweeps
 // Sinkhorn sweeps from beta = 0): T (the lane's rows), y (base-2 dual,
 // y_{N-1} = 0 implied), c (column sums of T) and res (their residual; 0 for
-// lanes past the end of the batch, which are thereby done).  The logits are
-// needed again only by the rare fallback sweep, which re-reads this lane's
-// rows; they do not stay in registers through the iteration.
+// lanes past the end of the batch, which are thereby done).  `wide` is set
+// when an entry of this T is below kTiny (logit spans of about 70 or more),
+// so that newton_iterate checks the converged T against its dual.  The logits
+// are needed again only by the rare fallback sweep and that check, which
+// re-read this lane's rows; they do not stay in registers through the
+// iteration.
 template <int N, typename IO, bool kPrefetch = false>
 __device__ __forceinline__ void newton_start(const Geometry<N, IO>& geo, uint4* lds, const IO* __restrict__ logits,
                                              float (&T)[Split<N>::K * N], float (&y)[N - 1], float (&c)[N],
-                                             float& res, const IO* __restrict__ prefetch_src = nullptr) {
+                                             float& res, bool& wide, const IO* __restrict__ prefetch_src = nullptr) {
     constexpr int M = N - 1, K = Split<N>::K;
     using G = Geometry<N, IO>;
     {
@@ -651,23 +781,26 @@ __device__ __forceinline__ void newton_start(const Geometry<N, IO>& geo, uint4* 
     }
     col_sums<N>(T, c);
     res = geo.valid() ? col_residual<N>(c) : 0.0f;   // lanes past the end are done
+    wide = geo.valid() && min_entry<N>(T) < kTiny;
 }
 
 // newton_start, then Newton's method to column-sum residual <= tol or max_iter
 // updates.  On return T is the lane's rows of the last iterate, y the dual
-// (base-2 units, y_{N-1} = 0 implied), res its residual; returns the number of
-// updates.
+// (base-2 units, y_{N-1} = 0 implied), res its residual, `sweeps` the number
+// of fallback sweeps among the updates; returns the number of updates.
 template <int N, typename IO, bool kPrefetch = false>
 __device__ __forceinline__ int newton_solve(const Geometry<N, IO>& geo, uint4* lds, const IO* __restrict__ logits,
                                             float tol, int max_iter, float (&T_out)[Split<N>::K * N],
-                                            float (&y_out)[N - 1], float& res_out,
+                                            float (&y_out)[N - 1], float& res_out, int& sweeps,
                                             const IO* __restrict__ prefetch_src = nullptr) {
     constexpr int M = N - 1, K = Split<N>::K;
     // the iteration works on locals, copied out at the end (keeps the loop in registers)
     float T[K * N], y[M], c[N], res;
-    newton_start<N, IO, kPrefetch>(geo, lds, logits, T, y, c, res, prefetch_src);
+    bool wide, checked = false;
+    newton_start<N, IO, kPrefetch>(geo, lds, logits, T, y, c, res, wide, prefetch_src);
     int it = 0;
-    newton_iterate<N, IO>(logits, geo.item(), tol, max_iter, T, y, c, res, it);
+    sweeps = 0;
+    newton_iterate<N, IO>(logits, WaveItem{geo.base}, tol, max_iter, T, y, c, res, it, wide, checked, sweeps);
 #pragma unroll
     for (int k = 0; k < K * N; ++k) T_out[k] = T[k];
 #pragma unroll
@@ -700,15 +833,20 @@ __device__ __forceinline__ void store_forward(const Geometry<N, IO>& geo, uint4*
 template <int N, typename IO, bool kStats>
 __global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(N == 4 ? 7 : 3)))
 newton_fwd_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, float* __restrict__ dual,
-                  int32_t* __restrict__ iters, int64_t B, float tol, int max_iter) {
+                  int32_t* __restrict__ iters, int32_t* __restrict__ fallbacks, int64_t B, float tol,
+                  int max_iter) {
     using G = Geometry<N, IO>;
     __shared__ uint4 lds[kWaves][G::Tile::kLdsChunks];
     const G geo(B);
     if (geo.nvalid == 0) return;
     float T[G::K * N], y[N - 1], res;
-    const int it = newton_solve<N, IO>(geo, lds[geo.wave], logits, tol, max_iter, T, y, res);
+    int sweeps;
+    const int it = newton_solve<N, IO>(geo, lds[geo.wave], logits, tol, max_iter, T, y, res, sweeps);
     store_forward<N, IO>(geo, lds[geo.wave], Tout, dual, T, y);
-    if (kStats && geo.valid() && geo.half() == 0) iters[geo.matrix()] = (res <= tol) ? it : -1;
+    if (kStats && geo.valid() && geo.half() == 0) {
+        iters[geo.matrix()] = (res <= tol) ? it : -1;
+        if (fallbacks) fallbacks[geo.matrix()] = sweeps;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -734,17 +872,22 @@ struct Gather {
     static constexpr int N = 4, M = N - 1, KN = Split<N>::K * N;
     static_assert(Split<N>::R == 1, "one matrix per lane");
     using G = Geometry<N, IO>;
-    // one handed-off state: T, y, c and the owner's lane in the workgroup; word j
-    // of record p sits at float j * kHandOff + p of the wave's region
+    // one handed-off state: T, y, c and a word holding the owner's lane in the
+    // workgroup (bits 0-7), its `wide` and `checked` flags (bits 8 and 9) and, when
+    // counted, its fallback sweeps so far (bits 10 and up); word j of record p sits
+    // at float j * kHandOff + p of the wave's region
     static constexpr int kWords = KN + M + N + 1;
     static constexpr int kRecordChunks = (kWords * kHandOff * 4 + 15) / 16;
     static constexpr int kRegion = G::Tile::kLdsChunks > kRecordChunks ? G::Tile::kLdsChunks : kRecordChunks;
 };
 
+// (the statistics variant, which also carries the counts, at six waves per SIMD
+// so that it does not spill)
 template <typename IO, bool kStats>
-__global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(7)))
+__global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kStats ? 6 : 7)))
 newton_fwd_gather_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, float* __restrict__ dual,
-                         int32_t* __restrict__ iters, int64_t B, float tol, int max_iter) {
+                         int32_t* __restrict__ iters, int32_t* __restrict__ fallbacks, int64_t B, float tol,
+                         int max_iter) {
     using Q = Gather<IO>;
     constexpr int N = Q::N, M = Q::M, KN = Q::KN;
     using G = typename Q::G;
@@ -753,11 +896,11 @@ newton_fwd_gather_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, f
     const G geo(B);
     const int first = max_iter < kFirstPass ? max_iter : kFirstPass;
     float T[KN], y[M], c[N], res = 0.0f;
-    int it = 0;
-    bool slow = false;
+    int it = 0, sweeps = 0;
+    bool slow = false, wide = false, checked = false;
     if (geo.nvalid > 0) {   // wave-uniform; waves past the end still reach the barrier
-        newton_start<N, IO>(geo, lds[geo.wave], logits, T, y, c, res);
-        newton_iterate<N, IO>(logits, geo.item(), tol, first, T, y, c, res, it);
+        newton_start<N, IO>(geo, lds[geo.wave], logits, T, y, c, res, wide);
+        newton_iterate<N, IO>(logits, WaveItem{geo.base}, tol, first, T, y, c, res, it, wide, checked, sweeps);
         slow = geo.valid() && res > tol && it < max_iter;
         const uint64_t mask = __ballot(slow);
         {
@@ -771,7 +914,10 @@ newton_fwd_gather_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, f
             for (int j = 0; j < M; ++j) beta[j] = y[j] * kLn2;
             beta[M] = 0.0f;
             store_dual<N>(dual, geo.matrix(), 0, beta);
-            if (kStats) iters[geo.matrix()] = (res <= tol) ? it : -1;
+            if (kStats) {
+                iters[geo.matrix()] = (res <= tol) ? it : -1;
+                if (fallbacks) fallbacks[geo.matrix()] = sweeps;
+            }
         }
         const int nslow = __popcll(mask);
         if (nslow > 0 && nslow <= kHandOff) {
@@ -786,7 +932,8 @@ newton_fwd_gather_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, f
                 for (int j = 0; j < M; ++j) rec[(KN + j) * kHandOff + p] = y[j];
 #pragma unroll
                 for (int j = 0; j < N; ++j) rec[(KN + M + j) * kHandOff + p] = c[j];
-                rec[(KN + M + N) * kHandOff + p] = __int_as_float((int)threadIdx.x);
+                rec[(KN + M + N) * kHandOff + p] = __int_as_float(
+                    (int)threadIdx.x | (wide ? 0x100 : 0) | (checked ? 0x200 : 0) | (kStats ? sweeps << 10 : 0));
             }
             slow = false;   // carried on by the workgroup
         }
@@ -828,13 +975,17 @@ newton_fwd_gather_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, f
             for (int j = 0; j < M; ++j) y[j] = rec[(KN + j) * kHandOff + p];
 #pragma unroll
             for (int j = 0; j < N; ++j) c[j] = rec[(KN + M + j) * kHandOff + p];
-            item = (int64_t)blockIdx.x * kBlock + __float_as_int(rec[(KN + M + N) * kHandOff + p]);
+            const int word = __float_as_int(rec[(KN + M + N) * kHandOff + p]);
+            item = (int64_t)blockIdx.x * kBlock + (word & 0xFF);
+            wide = (word & 0x100) != 0;
+            checked = (word & 0x200) != 0;
+            sweeps = word >> 10;
             res = col_residual<N>(c);
             it = first;
         }
     }
     if (slow) {
-        newton_iterate<N, IO>(logits, item, tol, max_iter, T, y, c, res, it);
+        newton_iterate<N, IO>(logits, LaneItem{item}, tol, max_iter, T, y, c, res, it, wide, checked, sweeps);
         uint4 w[G::C];
         Storage<IO>::template encode<KN>(T, w);
         uint4* q = reinterpret_cast<uint4*>(Tout) + item * G::C;
@@ -845,7 +996,10 @@ newton_fwd_gather_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, f
         for (int j = 0; j < M; ++j) beta[j] = y[j] * kLn2;
         beta[M] = 0.0f;
         store_dual<N>(dual, item, 0, beta);
-        if (kStats) iters[item] = (res <= tol) ? it : -1;
+        if (kStats) {
+            iters[item] = (res <= tol) ? it : -1;
+            if (fallbacks) fallbacks[item] = sweeps;
+        }
     }
 }
 
@@ -880,9 +1034,8 @@ __device__ __forceinline__ void implicit_grad(const float (&T)[Split<N>::K * N],
         for (int i = 1; i < K; ++i) s = fmaf(T[i * N + j], G[i * N + j] - mur[i], s);
         rhs[j] = P::sum(s);
     }
-    float h[Tri<N>::S], w[M];
-    hessian<N>(T, h);
-    SpdSolve<N>::run(h, rhs, w);
+    float w[M];
+    solve_delta<N>([&](float (&h)[Tri<N>::S]) { hessian<N>(T, h); }, rhs, w);
 #pragma unroll
     for (int i = 0; i < K; ++i) {
         float v = mur[i];
@@ -992,13 +1145,15 @@ fused_fwd_bwd_kernel(const IO* __restrict__ logits, const IO* __restrict__ dT, I
     float G[K * N], out[K * N];
     if constexpr (Gm::Tile::kStaged) {
         // dL/dT travels into LDS while the Newton iteration runs
-        newton_solve<N, IO, true>(geo, lds[geo.wave], logits, tol, max_iter, T, y, res, dT);
+        int sweeps;
+        newton_solve<N, IO, true>(geo, lds[geo.wave], logits, tol, max_iter, T, y, res, sweeps, dT);
         uint4 w[C];
         Gm::Tile::read_prefetched(lds[geo.wave], geo.lane, w);
         Storage<IO>::template decode<K * N>(w, G);
         store_forward<N, IO>(geo, lds[geo.wave], Tout, dual, T, y);
     } else {
-        newton_solve<N, IO>(geo, lds[geo.wave], logits, tol, max_iter, T, y, res);
+        int sweeps;
+        newton_solve<N, IO>(geo, lds[geo.wave], logits, tol, max_iter, T, y, res, sweeps);
         uint4 tg[C];
         Gm::Tile::fetch(geo.chunks(dT), geo.nvalid * C, geo.lane, tg);   // in flight while T is stored
         store_forward<N, IO>(geo, lds[geo.wave], Tout, dual, T, y);

@@ -24,8 +24,8 @@
  *     (b, i, j) of an [B, n, n] array is at offset (b*n + i)*n + j.
  *     The dual is [B, n] fp32: dual[b*n + j] = beta_j of matrix b, with the
  *     gauge beta_{n-1} = 0 (zero-based last column) stored explicitly.
- *   - Every pointer must be 16-byte aligned (iters of birkhoff_fwd_ex: 4-byte
- *     aligned); arrays must not overlap.
+ *   - Every pointer must be 16-byte aligned (iters and fallbacks of
+ *     birkhoff_fwd_ex: 4-byte aligned); arrays must not overlap.
  *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.
  *     Work is enqueued asynchronously on it; nothing synchronizes.
  *   - B == 0 is a no-op that returns BIRKHOFF_OK (pointers may then be NULL).
@@ -34,6 +34,12 @@
  *   - A matrix that does not reach `tol` within `max_iter` updates is not an
  *     error: its last iterate is written (see birkhoff_fwd_ex to detect it).
  *     Non-finite logits yield NaN in that matrix's outputs only.
+ *   - The backward passes solve eq (13)'s system with Delta, the Hessian at
+ *     the projection.  Where Delta is numerically singular (a projection within
+ *     rounding of a permutation on some rows and columns), dH does not depend
+ *     on the undetermined part of the solution; the system is then solved
+ *     rescaled and with a shift of 2^-22 of its trace, and at an exact
+ *     permutation (Delta = 0) the result is the exact dH = 0.
  *
  * Return codes: BIRKHOFF_OK or one of the negative BIRKHOFF_E* codes below;
  * birkhoff_strerror() describes them.
@@ -50,8 +56,10 @@ extern "C" {
 #define BIRKHOFF_OK 0
 #define BIRKHOFF_EINVAL (-1)  /* NULL pointer with B > 0, B < 0, unsupported n, tol <= 0 or NaN,
                                  max_iter < 1, iters < 1, or B too large for one launch */
-#define BIRKHOFF_EALIGN (-2)  /* a pointer is not 16-byte aligned (iters: not 4-byte aligned) */
-#define BIRKHOFF_ELAUNCH (-3) /* the HIP runtime reported an error at launch (hipGetLastError) */
+#define BIRKHOFF_EALIGN (-2)  /* a pointer is not 16-byte aligned (iters, fallbacks: not 4-byte aligned) */
+#define BIRKHOFF_ELAUNCH (-3) /* the HIP runtime rejected this call's kernel launch (the status that
+                                 hipLaunchKernel returned for it; an error left by an earlier HIP call
+                                 on the thread is neither reported here nor cleared) */
 
 /* Forward pass, fp32 storage.
  *   logits   [B, n, n] fp32, input H
@@ -68,10 +76,20 @@ extern "C" {
 int birkhoff_fwd(const float* logits, float* T, float* dual, int64_t B, int n,
                  float tol, int max_iter, void* stream);
 
-/* As birkhoff_fwd, and additionally writes iters[b] (int32, [B]): the number of
- * updates matrix b took to reach tol, or -1 when it did not reach tol within
- * max_iter updates (or its input was not finite).  iters must be non-NULL. */
-int birkhoff_fwd_ex(const float* logits, float* T, float* dual, int32_t* iters,
+/* As birkhoff_fwd, and additionally writes per-matrix statistics (int32, [B]):
+ *   iters[b]     the number of updates matrix b took to reach tol, or -1 when it
+ *                did not reach tol within max_iter updates (or its input was
+ *                not finite).  Must be non-NULL.
+ *   fallbacks[b] how many of those updates were the Sinkhorn-Knopp fallback
+ *                sweep, taken when no step size of the line search is accepted
+ *                (blog post, section 2.2).  May be NULL.
+ * A matrix counts as converged only if its T, rebuilt from the logits at the
+ * returned dual (rows Softmax(H_i. + beta), section 3.1), also meets tol
+ * whenever the iterate had entries below 2^-100 (logit spans of about 70 and
+ * more, where multiplicatively formed entries may have underflowed); the
+ * rebuilt T is then the one returned, and the iteration continues from it when
+ * it misses tol.  birkhoff_fwd computes the same T and dual. */
+int birkhoff_fwd_ex(const float* logits, float* T, float* dual, int32_t* iters, int32_t* fallbacks,
                     int64_t B, int n, float tol, int max_iter, void* stream);
 
 /* Backward pass, fp32 storage (section 4.1 eq (13), section 4.2).
@@ -206,7 +224,7 @@ int birkhoff_mix_bwd_bf16(const float* T, const uint16_t* x, const uint16_t* dy,
 /* Static description of a return code (never NULL). */
 const char* birkhoff_strerror(int code);
 
-/* ABI version, currently 1. */
+/* ABI version, currently 2 (version 1's birkhoff_fwd_ex had no fallbacks argument). */
 int birkhoff_abi_version(void);
 
 #ifdef __cplusplus

@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strerror(lib):
-    assert bp.birkhoff_abi_version() == 1
+    assert bp.birkhoff_abi_version() == 2
     for code in (0, -1, -2, -3, 12345):
         s = bp.birkhoff_strerror(code)
         assert isinstance(s, str) and s
@@ -74,7 +74,8 @@ def fwd(lib, *a):
 def test_forward_argument_checks(lib, B, n, tol, it, want):
     assert lib.birkhoff_fwd(P[0], P[1], P[2], B, n, tol, it, None) == want
     assert lib.birkhoff_fwd_bf16(P[0], P[1], P[2], B, n, tol, it, None) == want
-    assert lib.birkhoff_fwd_ex(P[0], P[1], P[2], P[3], B, n, tol, it, None) == want
+    assert lib.birkhoff_fwd_ex(P[0], P[1], P[2], P[3], None, B, n, tol, it, None) == want
+    assert lib.birkhoff_fwd_ex(P[0], P[1], P[2], P[3], P[3] + 64, B, n, tol, it, None) == want
 
 
 def test_null_and_misaligned_pointers(lib):
@@ -85,8 +86,10 @@ def test_null_and_misaligned_pointers(lib):
         assert lib.birkhoff_fwd(*ptrs, B, n, 1e-6, 50, None) == EINVAL
         ptrs[k] = P[k] + 4
         assert lib.birkhoff_fwd(*ptrs, B, n, 1e-6, 50, None) == EALIGN
-    assert lib.birkhoff_fwd_ex(P[0], P[1], P[2], None, B, n, 1e-6, 50, None) == EINVAL
-    assert lib.birkhoff_fwd_ex(P[0], P[1], P[2], P[3] + 2, B, n, 1e-6, 50, None) == EALIGN
+    assert lib.birkhoff_fwd_ex(P[0], P[1], P[2], None, None, B, n, 1e-6, 50, None) == EINVAL
+    assert lib.birkhoff_fwd_ex(P[0], P[1], P[2], None, P[3], B, n, 1e-6, 50, None) == EINVAL
+    assert lib.birkhoff_fwd_ex(P[0], P[1], P[2], P[3] + 2, None, B, n, 1e-6, 50, None) == EALIGN
+    assert lib.birkhoff_fwd_ex(P[0], P[1], P[2], P[3], P[3] + 66, B, n, 1e-6, 50, None) == EALIGN
     for k in range(4):
         ptrs = list(P)
         ptrs[k] = None

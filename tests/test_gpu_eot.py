@@ -311,3 +311,61 @@ def test_problems_beyond_32bit_offsets():
     check_backward(D[it], oracle.eot_bwd(T_ref, Gs, As, Bs, eta), Gs, T_ref, eta)
     del M, G, T, D, dual
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("eta", [1.0 / 16, 1.0 / 32])
+def test_forward_sharp_plans_verified(eta):
+    """Costs N(0, 1) at eta = 1/16 and 1/32: cost spans of 100 to 200 in units of
+    eta, so the plan's starting row softmaxes lose entries to fp32 underflow while
+    the iteration forms them multiplicatively; a converged plan with entries below
+    2^-100 is checked against its dual before it is accepted.  Every problem either
+    converges -- then it meets the forward gates against the oracle, where the
+    oracle certifies it (all but a few percent at eta = 1/32), and equals the plan
+    rebuilt from its dual, eq (4)'s optimality conditions -- or reports -1, exactly
+    where its float64 column residual exceeds tol/2.
+    The step rule crawls on the sharpest plans (no step size lowers the gradient
+    norm, and fallback sweeps move the dual slowly): the cap is 1000 updates, and
+    at eta = 1/32 a few percent of the problems still report -1 -- the method's
+    limit on such plans, which the test records rather than gates."""
+    w = workload(4, 6, eta=eta, seed=71)
+    B = 2048
+    M, a, b = W.make_eot(w, B=B)
+    print("eot sharp eta=%g" % eta, flush=True)
+    T, dual, iters = bp.eot_plan(dev(M), dev(a), dev(b), eta, max_iter=1000, with_iters=True)
+    torch.cuda.synchronize()
+    it = iters.cpu().numpy()
+    conv = it >= 0
+    assert conv.mean() >= 0.9, conv.mean()
+    M64, a64, b64 = M.astype(np.float64), a.astype(np.float64), b.astype(np.float64)
+    Tg, dg = f64(T), f64(dual)
+    assert np.isfinite(Tg).all()
+    assert residual(Tg, a64, b64)[conv].max() <= RES_TOL
+    assert np.abs(rebuilt(M64, a64, dg, eta) - Tg).max(axis=(1, 2))[conv].max() <= FWD_TOL
+    assert (np.abs(Tg.sum(1) - b64).max(1)[~conv] > 0.5e-6).all()
+    T_ref, _, st = oracle.eot_project(M64, a64, b64, eta)
+    cert = st >= 0
+    assert (~cert).sum() <= B // 20   # the float64 oracle's own Newton stalls on a few percent at eta = 1/32
+    err = np.abs(Tg - T_ref).max(axis=(1, 2))
+    assert err[conv & cert].max() <= FWD_TOL, err[conv & cert].max()
+    print("  unconverged %d, uncertified %d, max updates %d, err %.2e" % ((~conv).sum(), (~cert).sum(),
+                                                                         it.max(), err[conv & cert].max()))
+
+
+@pytest.mark.parametrize("n", [3, 4, 8])
+def test_backward_at_permutation_like_plans(n):
+    """eq (13) at plans that are a scaled permutation (one entry per row and column,
+    uniform marginals): Delta is zero there, and the exact dcost is zero since such
+    a plan does not move under small changes of the cost.  The kernel's solve
+    fails, falls back as documented (w = 0), and D is exactly zero, not NaN."""
+    rng = np.random.default_rng([n, 72])
+    B = 128
+    a = np.full(n, 1.0 / n, dtype=np.float32)
+    T = np.zeros((B, n, n), dtype=np.float32)
+    for k in range(B):
+        T[k, np.arange(n), rng.permutation(n)] = 1.0 / n
+    G = rng.standard_normal((B, n, n)).astype(np.float32)
+    D = bp.eot_plan_bwd(dev(T), dev(G), dev(a), 0.5)
+    torch.cuda.synchronize()
+    Dg = f64(D)
+    assert np.isfinite(Dg).all()
+    assert (Dg == 0.0).all(), np.abs(Dg).max()

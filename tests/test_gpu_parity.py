@@ -2,12 +2,16 @@
 same seeded inputs.  Needs an MI355X; run with -m gpu.
 
 Gates (fp32 storage):
-  forward   max |T - T_ref| <= 1e-5 over every entry;
+  forward   max |T - T_ref| <= 1e-5 over every entry, and the same distance between
+            T and the T rebuilt in float64 from (logits, dual) -- rows of the
+            projection are Softmax(H_i. + beta), so this checks the dual too;
   residual  max(|rowsum - 1|, |colsum - 1|) of the GPU's T, summed in float64, <= 1e-5;
   backward  per matrix max|dH - dH_ref| / max|dH_ref| <= 1e-4.
 bf16 storage adds half a bf16 ulp of the reference value to the T and dH gates
 (an fp32-exact answer must still be rounded once to be stored), and takes the
 residual on T rebuilt in float64 from the logits and the fp32 dual.
+On inputs whose projections come near permutations (beyond the five benchmark
+workloads) the backward is checked by backward_check instead.
 """
 import numpy as np
 import pytest
@@ -62,6 +66,8 @@ def rebuilt_T(H, dual):
 
 
 def run_fwd(w, Hs, stats=False):
+    """The forward; with stats, birkhoff_fwd_ex and its counts: iters is then the
+    pair (updates, fallback sweeps)."""
     B, n = Hs.shape[0], w.n
     H = as_storage(Hs, w)
     T = torch.empty_like(H)
@@ -70,8 +76,10 @@ def run_fwd(w, Hs, stats=False):
     if w.io == "bf16":
         bp.birkhoff_fwd_bf16(H, T, dual, w.tol, w.max_iter)
     elif stats:
-        iters = torch.empty(B, dtype=torch.int32, device=DEV)
-        bp.birkhoff_fwd_ex(H, T, dual, iters, w.tol, w.max_iter)
+        it = torch.empty(B, dtype=torch.int32, device=DEV)
+        fb = torch.empty(B, dtype=torch.int32, device=DEV)
+        bp.birkhoff_fwd_ex(H, T, dual, it, w.tol, w.max_iter, fallbacks=fb)
+        iters = (it, fb)
     else:
         bp.birkhoff_fwd(H, T, dual, w.tol, w.max_iter)
     return H, T, dual, iters
@@ -95,6 +103,9 @@ def check_forward(w, H64, T_gpu, dual_gpu, T_ref):
     else:
         assert err.max() <= FWD_TOL, err.max()
         res = residual(T_gpu).max()
+        # the dual is the projection's: T rebuilt from it is the returned T
+        dd = np.abs(T_gpu - rebuilt_T(H64, dual_gpu)).max()
+        assert dd <= FWD_TOL, dd
     assert res <= RES_TOL, res
     return err.max(), res
 
@@ -152,7 +163,7 @@ def test_parity_full_size_sampled(key):
     w = W.WORKLOADS[key]
     print("case full", key, w.B, flush=True)
     Hs = W.make_logits(w)
-    H, T, dual, _ = run_fwd(w, Hs)
+    H, T, dual, stats = run_fwd(w, Hs, stats=(key == "hard"))
     Gs = W.make_upstream(w) if w.upstream is not None else None
     dH = run_bwd(w, H, dual, Gs) if Gs is not None else None
     torch.cuda.synchronize()
@@ -170,6 +181,15 @@ def test_parity_full_size_sampled(key):
     assert res <= RES_TOL, res
     assert torch.isfinite(T.float()).all().item()
     idx = sample_indices(w.B)
+    if stats is not None:
+        # the hard inputs take the fallback sweep (blog post, section 2.2) on some
+        # matrices: all of them join the sample
+        its, fbs = stats[0].cpu().numpy(), stats[1].cpu().numpy()
+        assert (its >= 0).all() and ((fbs >= 0) & (fbs <= its)).all()
+        took = np.flatnonzero(fbs > 0)
+        assert took.size > 0, "no matrix took the fallback sweep"
+        print("  %d matrices took %d fallback sweeps" % (took.size, fbs.sum()))
+        idx = np.unique(np.concatenate([idx, took[:4096]]))
     it = torch.from_numpy(idx).to(DEV)
     H64 = W.decode_f64(Hs[idx])
     T_ref, _, st = oracle.project(H64, sk_cap=w.sk_cap)
@@ -621,7 +641,7 @@ def test_gathered_slow_lanes(max_iter):
         np.testing.assert_array_equal(it > 4, want_slow)
         T_ref, _, st = oracle.project(Hs.astype(np.float64))
         assert (st >= 0).all()
-        check_forward(W.WORKLOADS["hard"], Hs.astype(np.float64), host_f64(T), None, T_ref)
+        check_forward(W.WORKLOADS["hard"], Hs.astype(np.float64), host_f64(T), host_f64(dual), T_ref)
     else:
         assert (it[~want_slow] >= 0).all()
 
@@ -652,25 +672,81 @@ def test_gathered_slow_lanes_bf16(max_iter):
         assert (st >= 0).all()
         check_forward(w, H64, host_f64(T), dual.cpu().numpy().astype(np.float64), T_ref)
 
-def conditioned_backward_check(dH_gpu, dH_ref, T_ref):
-    """Backward gate on inputs whose projection is close to a permutation.  dH
-    depends on T through Delta^{-1} (eq 13), Delta = I - T_{-n}^T T_{-n}: an
-    entrywise change d of T changes each entry of Delta by at most 2d (columns of
-    T sum to one), so ||dDelta||_2 <= ||dDelta||_F <= 2(n-1)d (6d for n = 4), and
-    dH moves by up to 2(n-1)d / lambda_min(Delta) relative to its size to first
-    order.  With d the forward tolerance 1e-5 (the fp32 T, which the backward
-    starts from, is only that close to T_ref), the per-matrix gate is
-    1e-4 + 2(n-1)e-5 / lambda_min."""
-    Tm = T_ref[:, :, :-1]
-    n1 = Tm.shape[2]
-    Delta = np.eye(n1)[None] - np.matmul(Tm.transpose(0, 2, 1), Tm)
-    lam = np.linalg.eigvalsh(Delta)[:, 0]
-    scale = np.abs(dH_ref).max(axis=(1, 2))
-    rel = np.abs(dH_gpu - dH_ref).max(axis=(1, 2)) / scale
-    bound = BWD_TOL + 2 * n1 * FWD_TOL / np.maximum(lam, 1e-300)
-    assert (rel <= bound).all(), "worst excess %.3e (lambda_min %.3e)" % (
-        (rel / bound).max(), lam[np.argmax(rel / bound)])
-    return float(rel.max()), float((rel[lam > 0.1]).max(initial=0.0))
+U32 = 2.0 ** -24   # fp32 unit roundoff
+
+
+def delta_lambda_min(T):
+    """Smallest eigenvalue of eq (13)'s Delta at T, in float64: the Hessian
+    diag(c) - T_{-n}^T T_{-n} with its diagonal formed as sum_i T_ij sum_{l != j} T_il
+    (no cancellation, so that it keeps its digits near permutations)."""
+    m = T.shape[2] - 1
+    Gm = np.einsum("bij,bik->bjk", T, T)
+    D = -Gm[:, :m, :m].copy()
+    for j in range(m):
+        D[:, j, j] = Gm[:, j, :].sum(1) - Gm[:, j, j]
+    return np.linalg.eigvalsh(D)[:, 0]
+
+
+def colres(T):
+    return np.abs(T.sum(axis=1) - 1).max(axis=1)
+
+
+def backward_check(dH_gpu, T_used, G, T_ref, where=""):
+    """The backward on inputs whose projections come near permutations, where
+    eq (13) is ill-conditioned (the smallest eigenvalue lambda of Delta reaches
+    1e-11 on the pages' N(0, 10^2) inputs) and dH can be orders of magnitude
+    smaller than its terms G o T, which cancel.
+    (a) Against eq (13) evaluated by the oracle at the T the kernel used (T_used:
+        the stored T, or for birkhoff_bwd the T rebuilt from the dual), per matrix
+          |dH - dH_ref|_max <= 1e-4 |dH_ref|_max + |G o T|_max (8 n u + r) / lambda,
+        u = 2^-24 and r = max_j |c_j - 1| of T_used.  To first order the kernel's
+        rounding of Delta (a few ulps per entry, 2(n-1) 2u in norm) and of the
+        right-hand side mu_c - T^T mu_r (about 4 n u |G o T|) reach dH through
+        Delta^-1; the kernel's Delta is the Hessian at T_used, diag(c) - T^T T,
+        the oracle's the literal I - T^T T, and they differ by r.  Wherever lambda
+        exceeds about 3e-4 this gate is below 1e-2 |G o T| (typically far below).
+    (b) Against eq (13) at the reference projection T_ref, the gate widened by the
+        measured forward error d = |T_used - T_ref|_max: 2(n-1) d more in Delta's
+        norm, and 2 |G|_max d for the factor T of dH itself.
+    (c) At any conditioning: T does not change when a constant is added to a row
+        or a column of H, so every row and every column of the exact dH sums to
+        zero.  The kernel's column sums are the residual of its Delta solve --
+        rounding level, or, where Delta is below fp32 resolution and is solved
+        with 2^-20 (1 + tr Delta) added, that shift times w, which the shift keeps
+        within a few |G| -- and its row sums (1 - rowsum(T)) times O(|G| + |w|);
+        both stay within 1e-4 |G|_max.
+    The oracle's literal Delta = I - T^T T differs from the Hessian at T by
+    diag(c - 1), so it is positive definite only where lambda exceeds the
+    column residual r; below that (lambda under 1e-7 at the GPU's T, 1e-13 at
+    T_ref) its eq (13) is no reference, and those matrices are checked by (c)
+    only.  Returns (number of matrices where (a)'s gate is above 1e-2 |G o T|,
+    largest ratio of error to gate in (a))."""
+    n = T_used.shape[2]
+    gt = np.abs(G * T_used).max(axis=(1, 2))
+    lam = np.maximum(delta_lambda_min(T_used), 1e-300)
+    ref = oracle.bwd(T_used, G)
+    fin = np.isfinite(ref).all(axis=(1, 2)) & (lam > 2 * colres(T_used) + 1e-12)
+    err = np.abs(dH_gpu - ref).max(axis=(1, 2))
+    gate = 1e-4 * np.abs(ref).max(axis=(1, 2)) + gt * (8 * n * U32 + colres(T_used)) / lam
+    ratio = np.where(fin, err / gate, 0.0)
+    assert (ratio <= 1.0).all(), "%s (a): error %.3e above gate %.3e (lambda %.3e, |GoT| %.3e)" % (
+        where, err[np.argmax(ratio)], gate[np.argmax(ratio)], lam[np.argmax(ratio)], gt[np.argmax(ratio)])
+    ref2 = oracle.bwd(T_ref, G)
+    fin2 = fin & np.isfinite(ref2).all(axis=(1, 2)) & (delta_lambda_min(T_ref) > 2 * colres(T_ref) + 1e-12)
+    d = np.abs(T_used - T_ref).max(axis=(1, 2))
+    err2 = np.abs(dH_gpu - ref2).max(axis=(1, 2))
+    gate2 = (1e-4 * np.abs(ref2).max(axis=(1, 2)) + gt * (8 * n * U32 + colres(T_used) + 2 * (n - 1) * d) / lam
+             + 2 * np.abs(G).max(axis=(1, 2)) * d)
+    ratio2 = np.where(fin2, err2 / gate2, 0.0)
+    assert (ratio2 <= 1.0).all(), "%s (b): error %.3e above gate %.3e" % (
+        where, err2[np.argmax(ratio2)], gate2[np.argmax(ratio2)])
+    assert np.isfinite(dH_gpu).all(), where
+    gmax = np.abs(G).max(axis=(1, 2))
+    rows = np.abs(dH_gpu.sum(axis=2)).max(axis=1) / gmax
+    cols = np.abs(dH_gpu.sum(axis=1)).max(axis=1) / gmax
+    assert rows.max() <= 1e-4 and cols.max() <= 1e-4, "%s (c): row sums %.2e, column sums %.2e of |G|" % (
+        where, rows.max(), cols.max())
+    return int((gate > 1e-2 * gt).sum()), float(ratio.max())
 
 
 @pytest.mark.parametrize("B", [512, 8192])
@@ -678,29 +754,37 @@ def test_parity_pages_timing_shape(B):
     """The pages' timing inputs (4x4, N(0, 10^2) logits: farther from uniform than any
     benchmark workload) through the forward (gathering kernel), the backward and the
     one-launch forward + backward, against the oracle.  Many of these projections are
-    nearly permutations, where the backward is ill-conditioned (the smallest
-    eigenvalue of Delta goes down to 1e-11), so its gate widens with the condition
-    of Delta (conditioned_backward_check)."""
+    nearly permutations, where eq (13) is ill-conditioned; the backward is checked
+    by backward_check.  Some matrices take the fallback sweep (blog post, section
+    2.2); the counts say which, and they meet the gates like the rest."""
     w = W.pages_shape_workload(B)
     print("case pages shape", B, flush=True)
     Hs = W.make_logits(w)
     Gs = W.make_upstream(w)
     H64 = Hs.astype(np.float64)
-    H, T, dual, iters = run_fwd(w, Hs, stats=True)
+    H, T, dual, (iters, fb) = run_fwd(w, Hs, stats=True)
     dH = run_bwd(w, H, dual, Gs)
     _, _, T2, dual2, dH2 = run_fused(w, Hs, Gs)
+    dH3 = torch.empty_like(dH)
+    bp.birkhoff_bwd_from_T(T2, dev(Gs), dH3)
     torch.cuda.synchronize()
-    it = iters.cpu().numpy()
+    it, fbn = iters.cpu().numpy(), fb.cpu().numpy()
     assert (it >= 0).all(), (it < 0).sum()
+    assert ((fbn >= 0) & (fbn <= it)).all()
+    assert (fbn > 0).any(), "no matrix took the fallback sweep"
     assert torch.equal(T, T2) and torch.equal(dual, dual2)
     T_ref, _, st = oracle.project(H64, sk_cap=w.sk_cap)
     assert (st >= 0).all()
-    err, res = check_forward(w, H64, host_f64(T), None, T_ref)
-    dH_ref = oracle.bwd(T_ref, Gs.astype(np.float64))
-    rel, rel_wc = conditioned_backward_check(host_f64(dH), dH_ref, T_ref)
-    rel2, rel2_wc = conditioned_backward_check(host_f64(dH2), dH_ref, T_ref)
-    print("  max updates %d, fwd err %.2e, residual %.2e, bwd rel %.2e / fused %.2e "
-          "(where lambda_min > 0.1: %.2e / %.2e)" % (it.max(), err, res, rel, rel2, rel_wc, rel2_wc))
+    Tg, dg = host_f64(T), host_f64(dual)
+    err, res = check_forward(w, H64, Tg, dg, T_ref)
+    G64 = Gs.astype(np.float64)
+    loose, r1 = backward_check(host_f64(dH), rebuilt_T(H64, dg), G64, T_ref, "bwd")
+    _, r2 = backward_check(host_f64(dH2), Tg, G64, T_ref, "fused")
+    _, r3 = backward_check(host_f64(dH3), Tg, G64, T_ref, "from_T")
+    print("  max updates %d, %d matrices took %d fallback sweeps; fwd err %.2e (fallback matrices %.2e), "
+          "residual %.2e; bwd worst error/gate %.2f / %.2f / %.2f, %d of %d with a loose gate" % (
+              it.max(), (fbn > 0).sum(), fbn.sum(), err, np.abs(Tg - T_ref)[fbn > 0].max(), res, r1, r2, r3,
+              loose, B))
 
 
 @pytest.mark.parametrize("B", [1, 65, 257, 1000, 1320])
@@ -721,7 +805,7 @@ def test_gathered_ragged_batches_and_canaries(B):
     assert (Ibuf[:pad] == -7).all() and (Ibuf[pad + B:] == -7).all()
     assert (it.cpu().numpy() >= 0).all()
     T_ref, _, _ = oracle.project(Hs.astype(np.float64))
-    check_forward(W.WORKLOADS["hard"], Hs.astype(np.float64), host_f64(T), None, T_ref)
+    check_forward(W.WORKLOADS["hard"], Hs.astype(np.float64), host_f64(T), host_f64(dual), T_ref)
 
 
 def test_gathered_nonfinite_inputs_stay_in_their_matrix():
@@ -796,14 +880,14 @@ def test_graph_capture_and_replay():
 def test_parity_n8_large_logits():
     """8x8 logits N(0, s^2) with s per matrix from {1, 3, 5, 8} (the hard workload's
     scales at n = 8): the forward, the backward and the one-launch forward +
-    backward against the oracle (backward gate as conditioned_backward_check)."""
+    backward against the oracle (backward as backward_check)."""
     w = W.Workload(key="n8_sigma_mix", title="8x8 fp32, H~N(0,s^2), s per matrix from {1,3,5,8}",
                    B=4096 + 19, n=8, io="f32", logits=("sigma_mix", (1.0, 3.0, 5.0, 8.0)),
                    upstream=("normal", 1.0), passes="fwd+bwd", seed=9, max_iter=100, sk_cap=5_000)
     print("case n8 large logits", flush=True)
     Hs, Gs = W.make_logits(w), W.make_upstream(w)
     H64 = Hs.astype(np.float64)
-    H, T, dual, iters = run_fwd(w, Hs, stats=True)
+    H, T, dual, (iters, fb) = run_fwd(w, Hs, stats=True)
     dH = run_bwd(w, H, dual, Gs)
     _, _, T2, dual2, dH2 = run_fused(w, Hs, Gs)
     torch.cuda.synchronize()
@@ -812,12 +896,13 @@ def test_parity_n8_large_logits():
     assert torch.equal(T, T2) and torch.equal(dual, dual2)
     T_ref, _, st = oracle.project(H64, sk_cap=w.sk_cap)
     assert (st >= 0).all()
-    err, res = check_forward(w, H64, host_f64(T), None, T_ref)
-    dH_ref = oracle.bwd(T_ref, Gs.astype(np.float64))
-    rel, rel_wc = conditioned_backward_check(host_f64(dH), dH_ref, T_ref)
-    rel2, rel2_wc = conditioned_backward_check(host_f64(dH2), dH_ref, T_ref)
-    print("  max updates %d, fwd err %.2e, residual %.2e, bwd rel %.2e / fused %.2e "
-          "(where lambda_min > 0.1: %.2e / %.2e)" % (it.max(), err, res, rel, rel2, rel_wc, rel2_wc))
+    Tg, dg = host_f64(T), host_f64(dual)
+    err, res = check_forward(w, H64, Tg, dg, T_ref)
+    G64 = Gs.astype(np.float64)
+    loose, r1 = backward_check(host_f64(dH), rebuilt_T(H64, dg), G64, T_ref, "bwd")
+    _, r2 = backward_check(host_f64(dH2), Tg, G64, T_ref, "fused")
+    print("  max updates %d, fallback matrices %d, fwd err %.2e, residual %.2e, bwd worst error/gate %.2f / %.2f, "
+          "%d with a loose gate" % (it.max(), (fb.cpu().numpy() > 0).sum(), err, res, r1, r2, loose))
 
 
 def test_batch_beyond_32bit_offsets():
@@ -882,9 +967,9 @@ def sweep_logits(kind, B, n, rng):
 @pytest.mark.parametrize("kind", SWEEP_KINDS)
 def test_distribution_sweep(kind, n, io):
     """The one-launch forward + backward on logits of many shapes against the
-    oracle: forward and residual gates as everywhere, the backward gate widened
-    with the condition of Delta (conditioned_backward_check, bf16 adding half an
-    ulp), and the forward-only launch equal to the one-launch forward bit for bit.
+    oracle: forward and residual gates as everywhere, the backward by
+    backward_check (bf16: its part (a), with half an ulp for the stored rounding),
+    and the forward-only launch equal to the one-launch forward bit for bit.
     bf16 storage stops at scale 8: at N(0, 10^2) the fp32 dual, |beta| ~ 30, is
     itself rounded by ~2e-6, so T rebuilt from it misses the 1e-5 residual gate."""
     if io == "bf16" and kind == "normal:10":
@@ -910,12 +995,26 @@ def test_distribution_sweep(kind, n, io):
     T_ref, _, st = oracle.project(H64, sk_cap=5_000)
     assert (st >= 0).all()
     check_forward(w, H64, host_f64(T), dual.cpu().numpy().astype(np.float64), T_ref)
-    dH_ref = oracle.bwd(T_ref, G64)
     dHg = host_f64(dH)
-    if io == "bf16":   # the stored dH is rounded once more: half an ulp of slack per entry
-        dHg = dH_ref + np.sign(dHg - dH_ref) * np.maximum(np.abs(dHg - dH_ref) - half_ulp_bf16(dH_ref), 0.0)
-    rel, rel_wc = conditioned_backward_check(dHg, dH_ref, T_ref)
-    print("  bwd rel %.2e (where lambda_min > 0.1: %.2e)" % (rel, rel_wc))
+    if io == "bf16":
+        # backward_check's part (a) only: the kernel differentiates at its fp32
+        # iterate, which is not stored (the stored T is rounded to bf16); T rebuilt
+        # from (logits, dual) stands in for it, within 2e-6 of it (check_forward's
+        # rebuilt-T distance on fp32 storage stays below that), which widens the
+        # gate by 2(n-1) 2e-6 / lambda; and the stored dH is rounded once more, so
+        # half an ulp per entry is taken off the error
+        Tu = rebuilt_T(H64, host_f64(dual))
+        ref = oracle.bwd(Tu, G64)
+        dHg = ref + np.sign(dHg - ref) * np.maximum(np.abs(dHg - ref) - half_ulp_bf16(ref), 0.0)
+        gt = np.abs(G64 * Tu).max(axis=(1, 2))
+        gate = 1e-4 * np.abs(ref).max(axis=(1, 2)) + gt * (8 * n * U32 + colres(Tu) + 2 * (n - 1) * 2e-6) / np.maximum(
+            delta_lambda_min(Tu), 1e-300)
+        ratio = np.abs(dHg - ref).max(axis=(1, 2)) / gate
+        assert (ratio <= 1.0).all(), ratio.max()
+        print("  bwd worst error/gate %.2f" % ratio.max())
+    else:
+        loose, r = backward_check(dHg, host_f64(T), G64, T_ref, kind)
+        print("  bwd worst error/gate %.2f, %d of %d with a loose gate" % (r, loose, B))
 
 
 def test_binding_rejects_bad_arguments():
@@ -953,3 +1052,207 @@ def test_binding_rejects_bad_arguments():
     bp.birkhoff_fwd(H, T, dual)
     torch.cuda.synchronize()
     assert residual(host_f64(T)).max() <= RES_TOL
+
+
+# ------------------------------------------ large logit spans and underflow
+
+@pytest.mark.parametrize("n", [4, 8])
+@pytest.mark.parametrize("sigma", [16.0, 20.0, 30.0])
+def test_large_logit_spans(sigma, n):
+    """Logits N(0, sigma^2), beyond the pages' largest scale (10): spans reach 170,
+    so the starting row softmaxes have entries that underflow fp32, while the
+    iteration forms T multiplicatively.  Every matrix either converges -- and then
+    meets the forward gates against the oracle, equals the T rebuilt from its dual
+    and passes backward_check -- or reports -1, exactly where the float64 column
+    residual of its T exceeds tol/2 (the kernel decides in fp32).  The float64
+    oracle cannot certify a handful of the largest-scale matrices; those are
+    checked by eq (1)'s optimality conditions only (T = D1 exp(H) D2 with the
+    returned dual, marginals to 1e-5), and their number is bounded."""
+    B = 4096 + 19
+    rng = np.random.default_rng([int(sigma), n, 11])
+    H32 = (sigma * rng.standard_normal((B, n, n))).astype(np.float32)
+    G32 = rng.standard_normal((B, n, n)).astype(np.float32)
+    w = W.Workload(key="spans", title="N(0,%g^2)" % sigma, B=B, n=n, io="f32", logits=None, upstream=None,
+                   passes="fwd+bwd", seed=0, max_iter=100)
+    print("case spans sigma=%g n=%d" % (sigma, n), flush=True)
+    H, T, dual, (iters, fb) = run_fwd(w, H32, stats=True)
+    _, _, T2, dual2, dH = run_fused(w, H32, G32)
+    torch.cuda.synchronize()
+    assert torch.equal(T, T2) and torch.equal(dual, dual2)
+    H64, G64 = H32.astype(np.float64), G32.astype(np.float64)
+    Tg, dg = host_f64(T), host_f64(dual)
+    it, fbn = iters.cpu().numpy(), fb.cpu().numpy()
+    conv = it >= 0
+    assert conv.mean() >= 0.99
+    assert ((fbn >= 0) & (fbn <= np.where(conv, it, w.max_iter))).all()
+    assert np.isfinite(Tg).all()
+    # eq (1)'s optimality conditions for every converged matrix
+    assert residual(Tg)[conv].max() <= RES_TOL
+    assert np.abs(Tg - rebuilt_T(H64, dg)).max(axis=(1, 2))[conv].max() <= FWD_TOL
+    # -1 exactly where tol is not met
+    assert (colres(Tg)[~conv] > 0.5 * w.tol).all()
+    T_ref, _, st = oracle.project(H64, sk_cap=5_000)
+    cert = st >= 0
+    assert (~cert).sum() <= B // 200, (~cert).sum()
+    sel = conv & cert
+    err = np.abs(Tg - T_ref).max(axis=(1, 2))
+    assert err[sel].max() <= FWD_TOL, err[sel].max()
+    loose, r = backward_check(host_f64(dH)[sel], Tg[sel], G64[sel], T_ref[sel], "fused")
+    print("  unconverged %d, uncertified %d, fallback matrices %d, max updates %d, fwd err %.2e, "
+          "bwd worst error/gate %.2f (%d loose)" % ((~conv).sum(), (~cert).sum(), (fbn > 0).sum(), it.max(),
+                                                    err[sel].max(), r, loose))
+
+
+def underflow_batch(n, depth, B=256, seed=12):
+    """Logits whose starting row softmaxes lose entries that matter: rows 0 and 1
+    put `depth` in column 0 (so the projection must share column 0 between them,
+    and the dual pushes column 0 down by about depth), and hold 0 or -10 in the
+    other columns, whose entries at beta = 0 are e^-depth and e^-(depth + 10)
+    relative to the row: subnormal or zero in fp32 for depth >= 88.  In the
+    projection those entries carry about half of rows 0 and 1.  The other rows
+    are N(0, 1).  Each matrix gets its own random row and column order."""
+    rng = np.random.default_rng([n, int(depth), seed])
+    out = np.empty((B, n, n), dtype=np.float32)
+    for b in range(B):
+        H = rng.standard_normal((n, n))
+        H[0] = 0.0
+        H[1] = 0.0
+        H[0, 0] = H[1, 0] = depth
+        H[0, 1] = H[1, 2] = -10.0
+        out[b] = H[rng.permutation(n)][:, rng.permutation(n)]
+    return out
+
+
+@pytest.mark.parametrize("n", [4, 8])
+@pytest.mark.parametrize("depth", [60.0, 88.0, 95.0, 103.0, 120.0])
+def test_underflowed_start_is_verified(n, depth):
+    """underflow_batch: the starting T has lost entries (zero or subnormal), so these
+    lanes rebuild T from the logits at their dual when they converge and go on from
+    it.  Every matrix must converge to the oracle's projection, through the
+    forward (statistics variant and plain), the one-launch forward + backward and
+    the gathering path alike.  The step rule needs many updates here: while rows 0
+    and 1 both sit on column 0 the gradient norm does not decrease, no step size
+    is accepted, and each fallback sweep moves the dual by about log 2 -- so the
+    cap is 1000 updates."""
+    Hs = underflow_batch(n, depth)
+    B = Hs.shape[0]
+    w = W.Workload(key="underflow", title="", B=B, n=n, io="f32", logits=None, upstream=None, passes="fwd+bwd",
+                   seed=0, max_iter=1000)
+    print("case underflow n=%d depth=%g" % (n, depth), flush=True)
+    H, T, dual, (iters, fb) = run_fwd(w, Hs, stats=True)
+    _, T3, dual3, _ = run_fwd(w, Hs)
+    G32 = np.random.default_rng(5).standard_normal(Hs.shape).astype(np.float32)
+    _, _, T2, dual2, dH = run_fused(w, Hs, G32)
+    torch.cuda.synchronize()
+    assert torch.equal(T, T2) and torch.equal(dual, dual2) and torch.equal(T, T3) and torch.equal(dual, dual3)
+    it = iters.cpu().numpy()
+    assert (it >= 0).all(), (it < 0).sum()
+    print("  updates: mean %.1f max %d, fallback sweeps max %d" % (it.mean(), it.max(), fb.cpu().numpy().max()))
+    H64 = Hs.astype(np.float64)
+    T_ref, _, st = oracle.project(H64, sk_cap=5_000)
+    assert (st >= 0).all()
+    Tg = host_f64(T)
+    check_forward(w, H64, Tg, host_f64(dual), T_ref)
+    # the lost entries matter: some matrix has an entry of T_ref above 0.1 whose
+    # starting value in fp32 was below 2^-100
+    U = H64 - H64.max(axis=2, keepdims=True)
+    assert ((U < -100 * np.log(2)) & (T_ref > 0.1)).any() or depth < 88
+    backward_check(host_f64(dH), Tg, G32.astype(np.float64), T_ref, "fused")
+
+
+# ------------------------------------------- degenerate eq (13) systems
+
+def permutation_logits(n, c, B=64, seed=3):
+    """c times a random permutation matrix per matrix, plus N(0, 0.25^2): for large
+    c the projection is within e^-c of the permutation (exactly it, in fp32, for c
+    beyond about 104), where Delta is numerically singular or zero."""
+    rng = np.random.default_rng([n, int(c), seed])
+    H = 0.25 * rng.standard_normal((B, n, n))
+    for b in range(B):
+        H[b, np.arange(n), rng.permutation(n)] += c
+    return H.astype(np.float32)
+
+
+@pytest.mark.parametrize("n", [4, 8])
+@pytest.mark.parametrize("c", [30.0, 40.0, 60.0, 120.0])
+def test_backward_near_permutations(n, c):
+    """eq (13) where Delta is numerically singular: dH, whose exact value is within
+    O(e^-c |G|) of zero (T is locally constant at a permutation), stays finite and
+    below 1e-6 |G| through every backward entry point -- the dual-based backward,
+    the one from T, the one-launch forward + backward and autograd -- and is
+    exactly zero once T is an exact permutation in fp32."""
+    Hs = permutation_logits(n, c)
+    B = Hs.shape[0]
+    G32 = np.random.default_rng([n, int(c)]).standard_normal(Hs.shape).astype(np.float32)
+    H, G = dev(Hs), dev(G32)
+    print("case permutation n=%d c=%g" % (n, c), flush=True)
+    T, dual, dH1 = bp.project_fwd_bwd(H, G)
+    dH2 = bp.project_bwd(H, dual, G)
+    dH3 = torch.empty_like(G)
+    bp.birkhoff_bwd_from_T(T, G, dH3)
+    Ha = H.clone().requires_grad_(True)
+    (bp.BirkhoffProjection.apply(Ha) * G).sum().backward()
+    torch.cuda.synchronize()
+    gmax = np.abs(G32).max()
+    Tg = host_f64(T)
+    exact = bool(((Tg == 0.0) | (Tg == 1.0)).all())
+    for name, d in (("fused", dH1), ("bwd", dH2), ("from_T", dH3), ("autograd", Ha.grad)):
+        dh = host_f64(d)
+        assert np.isfinite(dh).all(), name
+        assert np.abs(dh).max() <= 1e-6 * gmax, (name, np.abs(dh).max())
+        if exact:
+            assert (dh == 0.0).all(), name
+    print("  T exact permutation: %s; max|dH| %.2e |G|" % (exact, np.abs(host_f64(dH1)).max() / gmax))
+
+
+@pytest.mark.parametrize("n", [4, 8])
+def test_backward_deflated_block(n):
+    """A matrix with one dominant logit (H_00 = 200, spread over the same rows and
+    columns elsewhere N(0, 1)) projects onto diag(1, T') up to e^-100, with T' the
+    projection of the trailing (n-1) x (n-1) block; its gradient is diag(0, dH')
+    with dH' eq (13) for that block.  The smaller problem is solved by the oracle
+    on its own, so the n x n kernels are pinned to an (n-1) x (n-1) reference, in
+    a case where the n x n Delta has a zero row and column."""
+    rng = np.random.default_rng([n, 77])
+    B = 512
+    Hs = rng.standard_normal((B, n, n)).astype(np.float32)
+    Hs[:, 0, 0] = 200.0
+    G32 = rng.standard_normal((B, n, n)).astype(np.float32)
+    H, G = dev(Hs), dev(G32)
+    print("case deflated n=%d" % n, flush=True)
+    T, dual, dH = bp.project_fwd_bwd(H, G, max_iter=100)
+    dH2 = torch.empty_like(G)
+    bp.birkhoff_bwd_from_T(T, G, dH2)
+    torch.cuda.synchronize()
+    Ts, _, st = oracle.project(Hs[:, 1:, 1:].astype(np.float64))
+    assert (st >= 0).all()
+    dHs = oracle.bwd(Ts, G32[:, 1:, 1:].astype(np.float64))
+    Tg = host_f64(T)
+    assert np.abs(Tg[:, 0, 0] - 1.0).max() <= FWD_TOL
+    assert np.abs(Tg[:, 0, 1:]).max() <= FWD_TOL and np.abs(Tg[:, 1:, 0]).max() <= FWD_TOL
+    assert np.abs(Tg[:, 1:, 1:] - Ts).max() <= FWD_TOL
+    # backward_check's gate (b) for the block: its T is within d of T' (the
+    # leakage into row and column 0 stops at the forward's tol)
+    Gb = G32[:, 1:, 1:].astype(np.float64)
+    gt = np.abs(Gb * Ts).max(axis=(1, 2))
+    d = np.abs(Tg[:, 1:, 1:] - Ts).max(axis=(1, 2))
+    gate = (BWD_TOL * np.abs(dHs).max(axis=(1, 2)) + 2 * np.abs(Gb).max(axis=(1, 2)) * d
+            + gt * (8 * n * U32 + colres(Tg) + 2 * (n - 1) * d) / delta_lambda_min(Ts))
+    for name, dd in (("fused", dH), ("from_T", dH2)):
+        dh = host_f64(dd)
+        assert np.abs(dh[:, 0, :]).max() <= 1e-6 * np.abs(G32).max(), name
+        assert np.abs(dh[:, :, 0]).max() <= 1e-6 * np.abs(G32).max(), name
+        err = np.abs(dh[:, 1:, 1:] - dHs).max(axis=(1, 2))
+        assert (err <= gate).all(), (name, (err / gate).max())
+    print("  block error/gate %.2f" % (np.abs(host_f64(dH)[:, 1:, 1:] - dHs).max(axis=(1, 2)) / gate).max())
+
+
+def test_double_backward_raises():
+    """The autograd functions' backward passes are computed by the kernels, not
+    from differentiable torch operations, so a second derivative through them is
+    refused rather than silently zero."""
+    H = torch.randn((64, 4, 4), device=DEV, requires_grad=True)
+    T = bp.BirkhoffProjection.apply(H)
+    (g,) = torch.autograd.grad((T * T).sum(), H, create_graph=True)
+    with pytest.raises(RuntimeError):
+        g.sum().backward()

@@ -63,7 +63,10 @@ def test_all_global_stores_are_non_temporal(asm):
 
 def test_n4_kernels_occupancy_and_no_spills(asm):
     ks = kernels(asm)
-    want = {"newton_fwd_gather_kernelIf": 7, "fused_fwd_bwd_kernelILi4Ef": 6, "implicit_bwd_kernelILi4Ef": 7}
+    # the gathering forward that the plain entry point runs keeps seven waves per SIMD;
+    # its statistics variant (iteration and fallback counts) six
+    want = {"newton_fwd_gather_kernelIfLb0E": 7, "newton_fwd_gather_kernelIfLb1E": 6,
+            "fused_fwd_bwd_kernelILi4Ef": 6, "implicit_bwd_kernelILi4Ef": 7}
     for key, occ in want.items():
         hits = [v for k, v in ks.items() if key in k]
         assert hits, key
