@@ -16,8 +16,13 @@ decides the small, launch-bound workload).
 Inputs are generated on the host from fixed seeds and copied to HBM before
 anything is timed.  Two complete input/output sets alternate between steps, so
 that a step never finds the previous step's data in the 256 MB last-level
-cache.  The timed region is `--steps` back-to-back steps between two HIP events
-on the stream the kernels run on; `value` is B / (time per step).
+cache.  Before the counted warm-up, steps run back to back for --settle-ms of
+wall time (400 ms by default), so that the engine clock has left its idle
+level whatever --warmup is.  The timed region is `--steps` back-to-back steps
+between two HIP events on the stream the kernels run on; `value` is
+B / (time per step).  `clock` records the settle phase and the engine clock
+that a probe kernel measures right behind the timed region, on the same
+stream (shader-clock cycles per tick of the constant-rate counter).
 
 The roofline figure is for the kernel with the longer average launch time
 (the fused kernel is the only one of its step); see roofline() for the VALU
@@ -32,7 +37,9 @@ same kernel sources (profiles/traffic_<workload>.json), or null when the
 kernels have changed since.
 
 The CPU baseline is the float64 oracle timed on a bounded sample of the same
-workload on this host's cores.
+workload on this host's cores (all of them, and one), with the CPU model and
+the time of its parts (the Sinkhorn reference to 1e-13, the Newton cross-check,
+the backward) on the same sample.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 300] [--workload train] [--path fused|separate]
 """
@@ -96,6 +103,93 @@ def roofline(workload: str, kernel: str, nbytes: float, ms: float, digest: str) 
     return out
 
 
+def settle(step, sets, ms: float):
+    """Runs `step` back to back (alternating the two sets) for `ms` milliseconds of
+    wall time before the counted warm-up.  The engine clock ramps up over tens of
+    milliseconds of load after idle (the first ~100 launches of the 86 us fused
+    step average 122 us), so a short counted warm-up alone would time the
+    VALU-bound kernels on a low clock.  Returns the number of steps run."""
+    import torch
+    t0 = time.perf_counter()
+    i = 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            step(sets[i % 2])
+            i += 1
+        torch.cuda.synchronize()
+    return i
+
+
+def timed_steps(fn, sets, K: int, stream, probe=None) -> float:
+    """K launches of fn (alternating the two sets) between two HIP events on
+    `stream`; returns ms per launch.  With `probe` (a ClockProbe) the clock probe
+    is enqueued right behind the end event, so that it measures the engine clock
+    the timed launches ended on (it runs after the region, outside its time)."""
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(K):
+        fn(sets[i % 2])
+    e1.record(stream)
+    if probe is not None:
+        probe.launch(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / K
+
+
+def clock_report(settle_steps, settle_ms, probe):
+    """The settle phase and the engine clock measured right after the timed region
+    (shader-clock cycles per constant-rate tick, birkhoff_clock_probe)."""
+    return {"settle_ms": settle_ms, "settle_steps": settle_steps,
+            "mhz_after_timed_region": round(probe.mhz(), 1), "peak_mhz": CLOCK_HZ / 1e6}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+ONE_CORE_SCRIPT = r"""
+import json, sys, time
+sys.path.insert(0, sys.argv[1])
+import oracle
+from birkhoff_projection_amd import workloads as W
+w = W.WORKLOADS[sys.argv[2]]
+B = int(sys.argv[3])
+H = W.decode_f64(W.make_logits(w, B=B))
+G = None if w.upstream is None else W.decode_f64(W.make_upstream(w, B=B))
+t0 = time.perf_counter()
+T, _, _ = oracle.project(H, sk_cap=w.sk_cap)
+if G is not None:
+    oracle.bwd(T, G)
+print(json.dumps({"seconds": time.perf_counter() - t0, "threads": oracle.threads()}))
+"""
+
+
+def one_core_baseline(w, per_matrix_s: float, target_s: float = 5.0):
+    """The same oracle on one core: a child process with OMP_NUM_THREADS=1 on a
+    prefix sized from the all-core rate to about target_s seconds."""
+    import os
+    import subprocess
+    Bs = int(min(w.B, max(256, target_s / max(per_matrix_s, 1e-9))))
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-c", ONE_CORE_SCRIPT, str(ROOT), w.key, str(Bs)], env=env,
+                       capture_output=True, text=True, timeout=300)
+    if r.returncode != 0:
+        return {"error": r.stderr.strip().splitlines()[-1] if r.stderr.strip() else "failed"}
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    return {"value": Bs / d["seconds"], "cores": d["threads"],
+            "sample": "the first %d matrices, %.1f s wall" % (Bs, d["seconds"])}
+
+
 def cpu_baseline(w, target_s: float = 10.0):
     """The float64 oracle (reference projection + eq (13) backward) on a bounded
     sample of the workload, on this host's cores."""
@@ -117,11 +211,29 @@ def cpu_baseline(w, target_s: float = 10.0):
     dt = run(probe)
     Bs = int(min(w.B, max(probe, probe * target_s / max(dt, 1e-6))))
     dt = run(Bs)
+    # the parts of the same work, on the same prefix and cores: the Sinkhorn
+    # reference to 1e-13 (capped) and the float64 Newton cross-check that
+    # oracle.project runs for every matrix, and the backward
+    H = W.decode_f64(W.make_logits(w, B=Bs))
+    parts = {}
+    t0 = time.perf_counter()
+    oracle.sinkhorn_tol(H, tol=1e-13, cap=w.sk_cap)
+    parts["sinkhorn_to_1e-13_s"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    T, _, _ = oracle.newton(H, tol=1e-13, max_iter=500)
+    parts["newton_cross_check_s"] = time.perf_counter() - t0
+    if not fwd_only:
+        G = W.decode_f64(W.make_upstream(w, B=Bs))
+        t0 = time.perf_counter()
+        oracle.bwd(T, G)
+        parts["eq13_backward_s"] = time.perf_counter() - t0
     return {"value": Bs / dt, "unit": "projections/s", "cores": oracle.threads(), "kind": "oracle",
             "sample": "the first %d matrices of the same seeded workload (%s), float64: Sinkhorn to 1e-13 "
                       "(cap %d sweeps) with a Newton cross-check%s; %.1f s wall"
                       % (Bs, "all of it" if Bs == w.B else "a prefix", w.sk_cap,
-                         "" if fwd_only else ", then the eq (13) backward", dt)}
+                         "" if fwd_only else ", then the eq (13) backward", dt),
+            "cpu_model": cpu_model(), "parts": parts,
+            "one_core": one_core_baseline(w, dt / Bs)}
 
 
 def eot_cpu_baseline(w, target_s: float = 10.0):
@@ -182,22 +294,17 @@ def eot_report(w, args, dev):
         run_fwd(s)
         run_bwd(s)
 
-    def timed(fn, K):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(K):
-            fn(sets[i % 2])
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / K
+    def timed(fn, K, probe=None):
+        return timed_steps(fn, sets, K, stream, probe)
 
+    settle_steps = settle(step, sets, args.settle_ms)
+    probe = bp.ClockProbe(dev)
     for i in range(args.warmup):
         step(sets[i % 2])
     torch.cuda.synchronize()
     K = args.steps
-    ms_step = timed(step, K)
+    ms_step = timed(step, K, probe)
+    clock = clock_report(settle_steps, args.settle_ms, probe)
     fwd_ms = timed(run_fwd, K)
     bwd_ms = timed(run_bwd, K)
     iters = torch.empty(B, dtype=torch.int32, device=dev)
@@ -227,6 +334,7 @@ def eot_report(w, args, dev):
         "kernels_hbm_frac": {k: v[1] / (v[0] * 1e-3) / 1e9 / HBM_PEAK_GBS for k, v in kern.items()},
         "newton": {"iterations_mean": float(it[it >= 0].mean()), "wave_max_mean": float(waves.max(1).mean()),
                    "unconverged": int((it < 0).sum())},
+        "clock": clock,
         "kernel_digest": digest,
     }
 
@@ -299,22 +407,17 @@ def mix_report(w, args, dev):
         run_fwd(s)
         run_bwd(s)
 
-    def timed(fn, K):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(K):
-            fn(sets[i % 2])
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / K
+    def timed(fn, K, probe=None):
+        return timed_steps(fn, sets, K, stream, probe)
 
+    settle_steps = settle(step, sets, args.settle_ms)
+    probe = bp.ClockProbe(dev)
     for i in range(args.warmup):
         step(sets[i % 2])
     torch.cuda.synchronize()
     K = args.steps
-    ms_step = timed(step, K)
+    ms_step = timed(step, K, probe)
+    clock = clock_report(settle_steps, args.settle_ms, probe)
     fwd_ms = timed(run_fwd, K)
     bwd_ms = timed(run_bwd, K)
     # context only: the same product through torch's batched matmul on the stored T
@@ -341,6 +444,7 @@ def mix_report(w, args, dev):
         "kernels_ms": {"birkhoff_fwd_mix": fwd_ms, "birkhoff_mix_bwd": bwd_ms},
         "kernels_hbm_frac": {k: v[1] / (v[0] * 1e-3) / 1e9 / HBM_PEAK_GBS for k, v in kern.items()},
         "torch_matmul_y_ms": torch_ms,
+        "clock": clock,
         "kernel_digest": digest,
     }
 
@@ -373,21 +477,16 @@ def forward_only_report(w, args, dev):
     def run_sk(st):
         bp.sinkhorn_fwd(st["H"], st["S"], 20, stream)
 
-    def timed(fn, K):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(K):
-            fn(sets[i % 2])
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / K
+    def timed(fn, K, probe=None):
+        return timed_steps(fn, sets, K, stream, probe)
 
+    settle_steps = settle(run_fwd, sets, args.settle_ms)
+    probe = bp.ClockProbe(dev)
     for i in range(args.warmup):
         run_fwd(sets[i % 2])
     K = args.steps
-    ms = timed(run_fwd, K)
+    ms = timed(run_fwd, K, probe)
+    clock = clock_report(settle_steps, args.settle_ms, probe)
     ms_sk = timed(run_sk, K)
     st = sets[0]
     iters = torch.empty(B, dtype=torch.int32, device=dev)
@@ -420,6 +519,7 @@ def forward_only_report(w, args, dev):
         "newton": dict(score(st["T"]), iterations_hist=hist, iterations_mean=float(it[it >= 0].mean()),
                        wave_max_mean=float(waves.max(1).mean()), unconverged=int((it < 0).sum())),
         "sinkhorn20": dict(score(st["S"]), ms_per_launch=ms_sk, value=B / (ms_sk * 1e-3)),
+        "clock": clock,
         "kernel_digest": digest,
     }
 
@@ -504,8 +604,10 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=300,
-                    help="untimed steps first; the engine clock needs tens of milliseconds of load to settle")
+    ap.add_argument("--warmup", type=int, default=300, help="untimed steps after the settle phase")
+    ap.add_argument("--settle-ms", type=float, default=400.0,
+                    help="milliseconds of untimed back-to-back steps before the counted warm-up: the engine "
+                         "clock needs tens of milliseconds of load to settle after idle")
     ap.add_argument("--workload", default="train", help="workload key (train is the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -675,24 +777,18 @@ def forward_backward_report(w, args, dev):
 
     step = run_fused if args.path == "fused" else step_separate
 
-    def timed(fn, K):
-        """K launches of fn (alternating the two sets) between two events; ms per launch."""
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(K):
-            fn(sets[i % 2])
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / K
+    def timed(fn, K, probe=None):
+        return timed_steps(fn, sets, K, stream, probe)
 
+    settle_steps = settle(step, sets, args.settle_ms)
+    probe = bp.ClockProbe(dev)
     for i in range(args.warmup):
         step(sets[i % 2])
     torch.cuda.synchronize()
 
     K = args.steps
-    ms_step = timed(step, K)             # the timed region: K whole steps
+    ms_step = timed(step, K, probe)      # the timed region: K whole steps
+    clock = clock_report(settle_steps, args.settle_ms, probe)
     other = step_separate if args.path == "fused" else run_fused
     ms_other = timed(other, K)           # the other form of the step, for comparison
     fwd_ms = timed(run_fwd, K)           # per-kernel launch times, same stream
@@ -750,6 +846,7 @@ def forward_backward_report(w, args, dev):
         "other_path": {"path": "separate" if args.path == "fused" else "fused", "ms_per_step": ms_other,
                        "value": B / (ms_other * 1e-3)},
         "graph_replay": {"path": args.path, "ms_per_step": ms_graph, "value": B / (ms_graph * 1e-3)},
+        "clock": clock,
         "kernel_digest": digest,
     }
     return out

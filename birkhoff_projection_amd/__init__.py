@@ -24,7 +24,7 @@ __all__ = [
     "birkhoff_fwd_bf16", "birkhoff_bwd_bf16", "birkhoff_fwd_bwd", "birkhoff_fwd_bwd_bf16",
     "birkhoff_eot_fwd", "birkhoff_eot_bwd",
     "birkhoff_fwd_mix", "birkhoff_fwd_mix_bf16", "birkhoff_mix_bwd", "birkhoff_mix_bwd_bf16",
-    "birkhoff_strerror", "birkhoff_abi_version",
+    "birkhoff_strerror", "birkhoff_abi_version", "ClockProbe",
     "project", "project_bwd", "project_fwd_bwd", "sinkhorn", "BirkhoffProjection",
     "eot_plan", "eot_plan_bwd", "EntropicOT",
     "project_mix", "project_mix_bwd", "ProjectMix",
@@ -78,6 +78,8 @@ def load_library():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ci
+    lib.birkhoff_clock_probe.argtypes = [vp, ci, ci, ctypes.POINTER(ci), vp]
+    lib.birkhoff_clock_probe.restype = ci
     lib.birkhoff_strerror.argtypes = [ci]
     lib.birkhoff_strerror.restype = ctypes.c_char_p
     lib.birkhoff_abi_version.argtypes = []
@@ -224,6 +226,31 @@ def birkhoff_bwd_from_T(T, dT, dH, stream=None) -> None:
     _mats(dH, "dH", torch.float32, B, n)
     dev = _same_device(T, dT, dH)
     _call("birkhoff_bwd_from_T", dev, _p(T), _p(dT), _p(dH), B, n, _stream_handle(stream, dev))
+
+
+class ClockProbe:
+    """The engine clock that kernels run at (birkhoff_clock_probe): `launch`
+    enqueues the probe on a stream; `mhz` reads its result once the stream has
+    passed it (it synchronises)."""
+
+    def __init__(self, device, blocks: int = 256, ticks: int = 2000):
+        torch = _torch()
+        self.device = torch.device(device)
+        self.blocks, self.ticks = int(blocks), int(ticks)
+        self.counts = torch.zeros(2 * self.blocks, dtype=torch.int64, device=self.device)
+        self.wall_khz = None
+
+    def launch(self, stream=None) -> None:
+        khz = ctypes.c_int(0)
+        _call("birkhoff_clock_probe", self.device, _p(self.counts), self.blocks, self.ticks, ctypes.byref(khz),
+              _stream_handle(stream, self.device))
+        self.wall_khz = khz.value
+
+    def mhz(self) -> float:
+        if self.wall_khz is None:
+            raise RuntimeError("ClockProbe.mhz() before launch()")
+        c = self.counts.view(-1, 2).cpu().double()
+        return float(c[:, 0].sum() / c[:, 1].sum()) * self.wall_khz / 1e3
 
 
 def sinkhorn_fwd(logits, T, iters: int = 20, stream=None) -> None:

@@ -172,9 +172,15 @@ struct WaveTile {
     static_assert(C == 2 || C == 4 || C == 8 || C == 16, "chunks per matrix");
     static constexpr bool kStaged = C <= 8;
     static constexpr int kLdsChunks = kStaged ? 64 * C : 1;   // LDS tile per wave, in 16-byte chunks
-    __device__ __forceinline__ static int slot(int m, int q) { return m * C + (q ^ ((m / (16 / C)) & (C - 1))); }
+    // (unsigned arithmetic: the divisions and remainders by powers of two are
+    // shifts and masks, and the chunk offsets k * 64 fold into immediates)
+    __device__ __forceinline__ static unsigned slot(unsigned m, unsigned q) {
+        return m * C + (q ^ ((m / (16 / C)) & (C - 1)));
+    }
     // chunk that a lane handles in access k: coalesced order when staged, its own chunk k otherwise
-    __device__ __forceinline__ static int chunk(int k, int lane) { return kStaged ? k * 64 + lane : lane * C + k; }
+    __device__ __forceinline__ static unsigned chunk(unsigned k, unsigned lane) {
+        return kStaged ? k * 64 + lane : lane * C + k;
+    }
 
     // Issue the global loads of one wave tile.  `src` points at the wave's first
     // matrix; `valid` (wave-uniform, >= 1) chunks exist.  A full tile loads
@@ -188,12 +194,12 @@ struct WaveTile {
         } else {
 #pragma unroll
             for (int k = 0; k < C; ++k) {
-                const int c = chunk(k, lane);
-                t[k] = stream_load(src + (c < valid ? c : valid - 1));
+                const unsigned c = chunk(k, lane);
+                t[k] = stream_load(src + (c < (unsigned)valid ? c : (unsigned)valid - 1));
             }
 #pragma unroll
             for (int k = 0; k < C; ++k) {
-                const bool keep = chunk(k, lane) < valid;
+                const bool keep = chunk(k, lane) < (unsigned)valid;
                 t[k].x = keep ? t[k].x : 0u;
                 t[k].y = keep ? t[k].y : 0u;
                 t[k].z = keep ? t[k].z : 0u;
@@ -207,7 +213,7 @@ struct WaveTile {
         if constexpr (kStaged) {
 #pragma unroll
             for (int k = 0; k < C; ++k) {
-                const int c = chunk(k, lane);
+                const unsigned c = chunk(k, lane);
                 lds[slot(c / C, c % C)] = t[k];
             }
             wave_lds_sync();
@@ -270,9 +276,9 @@ struct WaveTile {
         wave_lds_sync();
 #pragma unroll
         for (int k = 0; k < C; ++k) {
-            const int c = chunk(k, lane);
+            const unsigned c = chunk(k, lane);
             const uint4 v = lds[slot(c / C, c % C)];
-            if (c < valid && !((skip >> (c / C)) & 1u)) stream_store(dst + c, v);
+            if (c < (unsigned)valid && !((skip >> (c / C)) & 1u)) stream_store(dst + c, v);
         }
         wave_lds_sync();
     }
@@ -290,15 +296,15 @@ struct WaveTile {
             if (full) {
 #pragma unroll
                 for (int k = 0; k < C; ++k) {
-                    const int c = chunk(k, lane);
+                    const unsigned c = chunk(k, lane);
                     stream_store(dst + c, lds[slot(c / C, c % C)]);
                 }
             } else {
 #pragma unroll
                 for (int k = 0; k < C; ++k) {
-                    const int c = chunk(k, lane);
+                    const unsigned c = chunk(k, lane);
                     const uint4 v = lds[slot(c / C, c % C)];
-                    if (c < valid) stream_store(dst + c, v);
+                    if (c < (unsigned)valid) stream_store(dst + c, v);
                 }
             }
             wave_lds_sync();
@@ -309,8 +315,8 @@ struct WaveTile {
             } else {
 #pragma unroll
                 for (int k = 0; k < C; ++k) {
-                    const int c = chunk(k, lane);
-                    if (c < valid) stream_store(dst + c, own[k]);
+                    const unsigned c = chunk(k, lane);
+                    if (c < (unsigned)valid) stream_store(dst + c, own[k]);
                 }
             }
         }

@@ -631,13 +631,115 @@ __device__ __forceinline__ void load_own(const IO* __restrict__ p, int64_t item,
 // lane whose check falls on its last allowed update ends with count -1 if the
 // rebuilt T misses tol.  Lanes whose entries all stay above kTiny -- every
 // benchmark input -- take none of this.
+// One update of newton_iterate: the Newton step with the line search, or the
+// fallback sweep when no step size is accepted.
 template <int N, typename IO, typename Item>
+__device__ __forceinline__ void newton_update(const IO* __restrict__ logits, Item item, float (&T)[Split<N>::K * N],
+                                              float (&y)[N - 1], float (&c)[N], float& res, int& it, int& sweeps) {
+    constexpr int M = N - 1, K = Split<N>::K;
+    float g[M], r[M], d[M];
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+        g[j] = c[j] - 1.0f;
+        r[j] = -g[j];
+    }
+    float gn2 = g[0] * g[0];
+#pragma unroll
+    for (int j = 1; j < M; ++j) gn2 = fmaf(g[j], g[j], gn2);
+    float h[Tri<N>::S];
+    hessian<N>(T, h);
+    damp<N>(h);
+    const bool ok = SpdSolve<N>::run(h, r, d);   // d = -H^{-1} g
+
+    bool accepted = false;
+    if (ok) {
+        for (int k = 0; k < 5; ++k) {
+            const float gam = step_size(k);
+            float s[M], e[M], rr[K], ct[N];
+#pragma unroll
+            for (int j = 0; j < M; ++j) s[j] = gam * d[j];
+            float noise;
+            const float df = trial_point<N>(T, s, e, rr, ct, noise);
+            float gt2 = (ct[0] - 1.0f) * (ct[0] - 1.0f);
+#pragma unroll
+            for (int j = 1; j < M; ++j) gt2 = fmaf(ct[j] - 1.0f, ct[j] - 1.0f, gt2);
+            // the objective must not increase beyond what fp32 can resolve, and
+            // the gradient norm must decrease
+            if (df < noise && gt2 < gn2) {
+#pragma unroll
+                for (int j = 0; j < M; ++j) y[j] = fmaf(s[j], kLog2e, y[j]);
+                accept_trial<N>(T, e, rr);
+#pragma unroll
+                for (int j = 0; j < N; ++j) c[j] = ct[j];
+                accepted = true;
+                break;
+            }
+        }
+    }
+    if (!accepted) {
+        float L[K * N];
+        load_own<N, IO>(logits, item.get(), L);
+#pragma unroll
+        for (int k = 0; k < K * N; ++k) L[k] *= kLog2e;
+        sinkhorn_sweep<N>(L, y);
+        softmax_rows<N, K>(L, y, T);
+        col_sums<N>(T, c);
+        ++sweeps;
+    }
+    ++it;
+    res = col_residual<N>(c);
+}
+
+// The check of a converged lane (see newton_iterate): true when the lane is done;
+// otherwise T has been rebuilt from the logits at its dual, with its column sums
+// and residual, and the iteration goes on from it.
+template <int N, typename IO, typename Item>
+__device__ __forceinline__ bool converged_or_rebuilt(const IO* __restrict__ logits, Item item, float tol,
+                                                     float (&T)[Split<N>::K * N], const float (&y)[N - 1],
+                                                     float (&c)[N], float& res, bool& wide, bool& checked) {
+    constexpr int K = Split<N>::K;
+    if (!(res <= tol) || checked || (!wide && min_entry<N>(T) >= kTiny)) return true;
+    checked = true;
+    wide = false;
+    float L[K * N];
+    load_own<N, IO>(logits, item.get(), L);
+#pragma unroll
+    for (int k = 0; k < K * N; ++k) L[k] *= kLog2e;
+    softmax_rows<N, K>(L, y, T);
+    col_sums<N>(T, c);
+    res = col_residual<N>(c);
+    return false;
+}
+
+template <int N, typename IO, bool kOneLoop = (Split<N>::R == 1), typename Item>
 __device__ __forceinline__ void newton_iterate(const IO* __restrict__ logits, Item item, float tol, int max_iter,
                                                float (&T)[Split<N>::K * N], float (&y)[N - 1], float (&c)[N],
                                                float& res, int& it, bool& wide, bool& checked, int& sweeps) {
-    constexpr int M = N - 1, K = Split<N>::K;
-    for (;;) {
-        while (res > tol && it < max_iter) {
+    // The same iteration in two loop shapes, chosen by measurement per kernel.
+    // kOneLoop: a single loop with the check on its exit path, and the update
+    // written out in it (the same steps as newton_update; called through a
+    // function, inlined or not, the update costs one matrix per lane a wave of
+    // occupancy); an inner loop around the check makes the compiler copy T at
+    // every update.  Otherwise the updates run in an inner loop and the check
+    // after it: lane pairs spill in the single loop, and the gather kernel,
+    // which holds two copies of the iteration, runs faster this way.
+    if constexpr (kOneLoop) {
+        constexpr int K = Split<N>::K;
+        for (;;) {
+            if (!(res > tol && it < max_iter)) {
+                if (!(res <= tol) || checked || (!wide && min_entry<N>(T) >= kTiny)) break;
+                checked = true;
+                wide = false;
+                float L[K * N];
+                load_own<N, IO>(logits, item.get(), L);
+#pragma unroll
+                for (int k = 0; k < K * N; ++k) L[k] *= kLog2e;
+                softmax_rows<N, K>(L, y, T);
+                col_sums<N>(T, c);
+                res = col_residual<N>(c);
+                continue;
+            }
+            constexpr int M = N - 1;
             float g[M], r[M], d[M];
 #pragma unroll
             for (int j = 0; j < M; ++j) {
@@ -690,17 +792,11 @@ __device__ __forceinline__ void newton_iterate(const IO* __restrict__ logits, It
             ++it;
             res = col_residual<N>(c);
         }
-        // converged (or out of updates, or not finite): a suspect lane is rebuilt once
-        if (!(res <= tol) || checked || (!wide && min_entry<N>(T) >= kTiny)) break;
-        checked = true;
-        wide = false;
-        float L[K * N];
-        load_own<N, IO>(logits, item.get(), L);
-#pragma unroll
-        for (int k = 0; k < K * N; ++k) L[k] *= kLog2e;
-        softmax_rows<N, K>(L, y, T);
-        col_sums<N>(T, c);
-        res = col_residual<N>(c);
+    } else {
+        for (;;) {
+            while (res > tol && it < max_iter) newton_update<N, IO>(logits, item, T, y, c, res, it, sweeps);
+            if (converged_or_rebuilt<N, IO>(logits, item, tol, T, y, c, res, wide, checked)) break;
+        }
     }
 }
 
@@ -900,7 +996,7 @@ newton_fwd_gather_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, f
     bool slow = false, wide = false, checked = false;
     if (geo.nvalid > 0) {   // wave-uniform; waves past the end still reach the barrier
         newton_start<N, IO>(geo, lds[geo.wave], logits, T, y, c, res, wide);
-        newton_iterate<N, IO>(logits, WaveItem{geo.base}, tol, first, T, y, c, res, it, wide, checked, sweeps);
+        newton_iterate<N, IO, false>(logits, WaveItem{geo.base}, tol, first, T, y, c, res, it, wide, checked, sweeps);
         slow = geo.valid() && res > tol && it < max_iter;
         const uint64_t mask = __ballot(slow);
         {
@@ -985,7 +1081,7 @@ newton_fwd_gather_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, f
         }
     }
     if (slow) {
-        newton_iterate<N, IO>(logits, LaneItem{item}, tol, max_iter, T, y, c, res, it, wide, checked, sweeps);
+        newton_iterate<N, IO, false>(logits, LaneItem{item}, tol, max_iter, T, y, c, res, it, wide, checked, sweeps);
         uint4 w[G::C];
         Storage<IO>::template encode<KN>(T, w);
         uint4* q = reinterpret_cast<uint4*>(Tout) + item * G::C;

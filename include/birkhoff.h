@@ -221,6 +221,22 @@ int birkhoff_mix_bwd(const float* T, const float* x, const float* dy, float* dx,
 int birkhoff_mix_bwd_bf16(const float* T, const uint16_t* x, const uint16_t* dy, uint16_t* dx, float* dH, int64_t B,
                           int n, int64_t C, void* stream);
 
+/* ---- measurement aid (not part of the method) ------------------------------
+ *
+ * birkhoff_clock_probe: the engine clock that kernels run at, for benchmark
+ * reports (the driver's sampled clock can lag the load).  Enqueues on `stream`
+ * `blocks` workgroups of one wave each; workgroup k writes
+ * counts[2k] = shader-clock cycles and counts[2k+1] = ticks of the
+ * constant-rate counter over the same interval of about `ticks` ticks.  The
+ * clock in kHz is sum(counts[even]) / sum(counts[odd]) * *wall_khz, where
+ * *wall_khz (written before return, on the host) is the constant counter's
+ * rate on the current device.  counts: device memory of 2*blocks uint64,
+ * 16-byte aligned, owned by the caller, valid once the stream has reached the
+ * probe.  1 <= blocks <= 65536, 1 <= ticks <= 2^20.  Returns BIRKHOFF_EINVAL
+ * for a NULL pointer or a size out of range, BIRKHOFF_EALIGN for a misaligned
+ * counts, BIRKHOFF_ELAUNCH when the device query or the launch fails. */
+int birkhoff_clock_probe(uint64_t* counts, int blocks, int ticks, int* wall_khz, void* stream);
+
 /* Static description of a return code (never NULL). */
 const char* birkhoff_strerror(int code);
 

@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
               "birkhoff_fwd_bf16", "birkhoff_bwd_bf16", "birkhoff_fwd_bwd", "birkhoff_fwd_bwd_bf16",
               "birkhoff_bwd_from_T", "birkhoff_eot_fwd", "birkhoff_eot_bwd",
               "birkhoff_fwd_mix", "birkhoff_fwd_mix_bf16", "birkhoff_mix_bwd", "birkhoff_mix_bwd_bf16",
-              "birkhoff_strerror", "birkhoff_abi_version"):
+              "birkhoff_strerror", "birkhoff_abi_version", "birkhoff_clock_probe"):
         assert n in names
 
 
@@ -256,6 +256,46 @@ def test_mix_null_and_misaligned_pointers(lib):
         ptrs[k] = R[k] + 8
         assert lib.birkhoff_mix_bwd(*ptrs, 9, 4, 64, None) == EALIGN
         assert lib.birkhoff_mix_bwd_bf16(*ptrs, 9, 4, 64, None) == EALIGN
+
+
+def test_clock_probe_argument_checks(lib):
+    khz = ctypes.c_int(0)
+    ref = ctypes.byref(khz)
+    assert lib.birkhoff_clock_probe(None, 4, 100, ref, None) == EINVAL
+    assert lib.birkhoff_clock_probe(A, 4, 100, None, None) == EINVAL
+    for blocks, ticks in ((0, 100), (-1, 100), (65537, 100), (4, 0), (4, -5), (4, (1 << 20) + 1)):
+        assert lib.birkhoff_clock_probe(A, blocks, ticks, ref, None) == EINVAL, (blocks, ticks)
+    assert lib.birkhoff_clock_probe(A + 8, 4, 100, ref, None) == EALIGN
+
+
+ELAUNCH_SCRIPT = r"""
+import ctypes, sys
+sys.path.insert(0, sys.argv[1])
+import birkhoff_projection_amd as bp
+lib = bp.load_library()
+A = 1 << 20
+khz = ctypes.c_int(0)
+codes = [lib.birkhoff_fwd(A, A + 4096, A + 8192, 5, 4, 1e-6, 50, None),
+         lib.birkhoff_fwd_bwd(A, A + 4096, A + 8192, A + 12288, A + 16384, 5, 8, 1e-6, 50, None),
+         lib.sinkhorn_fwd(A, A + 4096, 5, 4, 20, None),
+         lib.birkhoff_clock_probe(A, 4, 100, ctypes.byref(khz), None)]
+print(" ".join(map(str, codes)))
+"""
+
+
+@pytest.mark.skipif(pathlib.Path("/dev/kfd").exists(),
+                    reason="needs a machine without a GPU: the valid calls here use fake addresses, "
+                           "which only a launch that fails may be given")
+def test_launch_failure_is_reported():
+    """Calls that pass every argument check reach the launch; where the HIP
+    runtime has no device to launch on, each returns BIRKHOFF_ELAUNCH (the
+    launch's own status) instead of crashing or reporting success."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, "-c", ELAUNCH_SCRIPT, str(ROOT)], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.split() == ["-3"] * 4, r.stdout
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
