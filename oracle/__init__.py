@@ -72,8 +72,6 @@ def _load():
     lib.oracle_project.argtypes = [dp, i64, ci, ci, dp, dp, ip]
     lib.oracle_bwd.restype = ci
     lib.oracle_bwd.argtypes = [dp, dp, i64, ci, dp]
-    lib.oracle_residuals.restype = ci
-    lib.oracle_residuals.argtypes = [dp, i64, ci, dp]
     lib.oracle_eot_sinkhorn_tol.restype = ci
     lib.oracle_eot_sinkhorn_tol.argtypes = [dp, dp, dp, i64, ci, ci, cd, cd, ci, dp, dp, ip, ip]
     lib.oracle_eot_newton.restype = ci
@@ -82,8 +80,6 @@ def _load():
     lib.oracle_eot_project.argtypes = [dp, dp, dp, i64, ci, ci, cd, ci, dp, dp, ip]
     lib.oracle_eot_bwd.restype = ci
     lib.oracle_eot_bwd.argtypes = [dp, dp, dp, dp, i64, ci, ci, cd, dp]
-    lib.oracle_eot_residuals.restype = ci
-    lib.oracle_eot_residuals.argtypes = [dp, dp, dp, i64, ci, ci, dp]
     lib.oracle_mix.restype = ci
     lib.oracle_mix.argtypes = [dp, dp, i64, ci, i64, dp]
     lib.oracle_mix_bwd.restype = ci
@@ -181,15 +177,6 @@ def bwd(T, G):
     return dH
 
 
-def residuals(T):
-    """Per-matrix max(|rowsum-1|, |colsum-1|), summed in double."""
-    T = _mat(T)
-    B, n, _ = T.shape
-    r = np.empty(B)
-    _check(_load().oracle_residuals(_p(T), B, n, _p(r)), "residuals")
-    return r
-
-
 # ---------------------------------------------------------------------------
 # General small entropic OT: cost M [B, n, m], marginals a [B, n], b [B, m]
 # (or [n], [m], shared by every problem), regularisation eta > 0.
@@ -254,14 +241,6 @@ def eot_bwd(T, G, a, b, eta: float = 1.0):
     D = np.empty_like(T)
     _check(_load().oracle_eot_bwd(_p(T), _p(G), _p(a), _p(b), B, n, m, float(eta), _p(D)), "eot_bwd")
     return D
-
-
-def eot_residuals(T, a, b):
-    """Per-problem max(|T 1 - a|, |T^T 1 - b|), summed in double."""
-    T, a, b, B, n, m = _eot_args(T, a, b)
-    r = np.empty(B)
-    _check(_load().oracle_eot_residuals(_p(T), _p(a), _p(b), B, n, m, _p(r)), "eot_residuals")
-    return r
 
 
 # ---------------------------------------------------------------------------

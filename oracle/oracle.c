@@ -778,16 +778,6 @@ int oracle_bwd(const double *T, const double *G, int64_t B, int n, double *dH)
     return (int)(bad > 0x7fffffff ? 0x7fffffff : bad);
 }
 
-/* Marginal residual max(|rowsum - 1|, |colsum - 1|) of each matrix, summed in
- * double; used to score a projected output against the constraint of B_n. */
-int oracle_residuals(const double *T, int64_t B, int n, double *res)
-{
-    if (bad_args(B, n, T) || (B > 0 && !res)) return -1;
-#pragma omp parallel for schedule(static)
-    for (int64_t b = 0; b < B; ++b) res[b] = marginal_residual(T + b * n * n, n);
-    return 0;
-}
-
 /* ---- general entropic OT: a [B, n], b [B, m], M / T / G / D [B, n, m] ---- */
 
 static int eot_bad_args(int64_t B, int n, int m, double eta, const void *p)
@@ -867,14 +857,6 @@ int oracle_eot_bwd(const double *T, const double *G, const double *a, const doub
     for (int64_t q = 0; q < B; ++q)
         if (eot_bwd_one(T + q * n * m, G + q * n * m, a + q * n, b + q * m, n, m, eta, D + q * n * m) != 0) ++bad;
     return (int)(bad > 0x7fffffff ? 0x7fffffff : bad);
-}
-
-int oracle_eot_residuals(const double *T, const double *a, const double *b, int64_t B, int n, int m, double *res)
-{
-    if (eot_bad_args(B, n, m, 1.0, T) || (B > 0 && (!a || !b || !res))) return -1;
-#pragma omp parallel for schedule(static)
-    for (int64_t q = 0; q < B; ++q) res[q] = eot_marginal_residual(T + q * n * m, a + q * n, b + q * m, n, m);
-    return 0;
 }
 
 /* ------------------------------------------------------------------ */
