@@ -364,7 +364,7 @@ struct Lanes {
     int64_t base;             // first problem of this wave
     __device__ __forceinline__ explicit Lanes(int64_t B) {
         lane = threadIdx.x & 63;
-        wave = threadIdx.x >> 6;
+        wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: base goes to SGPRs
         base = ((int64_t)blockIdx.x * W + wave) * 64;
         const int64_t left = B - base;
         nvalid = __builtin_amdgcn_readfirstlane(left <= 0 ? 0 : left >= 64 ? 64 : (int)left);

@@ -160,7 +160,7 @@ project_mix_kernel(const float* __restrict__ logits, const XT* __restrict__ x, f
     static_assert(kTokens == kWaves, "one token per wave");
     __shared__ uint4 tile[Gm::Tile::kLdsChunks];
     __shared__ float Ts[kTokens * kTs];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int64_t first = (int64_t)blockIdx.x * kTokens;
     const int64_t left = B - first;
     const int ntok = left >= kTokens ? kTokens : (int)left;
@@ -252,7 +252,7 @@ __global__ void __launch_bounds__(kBlock)
 mix_bwd_kernel(const float* __restrict__ Tin, const XT* __restrict__ x, const XT* __restrict__ dy,
                XT* __restrict__ dx, float* __restrict__ dH, int64_t B, int64_t Q) {
     __shared__ float dTs[kTokens * kTs];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int64_t first = (int64_t)blockIdx.x * kTokens;
     const int64_t left = B - first;
     const int ntok = left >= kTokens ? kTokens : (int)left;

@@ -34,8 +34,20 @@
 namespace birk {
 
 constexpr int kBlock = 256;  // threads per workgroup (4 waves of 64)
-// Sinkhorn-Knopp sweeps that give Newton's starting point (not counted as updates)
+// Sinkhorn-Knopp sweeps that give Newton's starting point (not counted as
+// updates): kStartSweeps always, then up to kMoreSweeps more while the lane's
+// column-sum residual is above kSweepOn.  A sweep costs a fifth of an update,
+// and a wave runs until its slowest lane is done: on logits of large magnitude
+// the far lanes hold their waves for several updates, on moderate ones
+// (residuals of a few 1e-2 after three sweeps) no lane takes the extra sweeps.
+// The decision is the lane's own, so a matrix's result does not depend on the
+// other matrices of the batch.
+// Measured on the hard-conditioning workload (sigma in {1, 3, 5, 8}): 84.6 us
+// with none, 72.9 with up to 3, 64.5 with up to 8, 65.4 with up to 12; the
+// moderate workloads are unchanged within 1 %.
 constexpr int kStartSweeps = 3;
+constexpr int kMoreSweeps = 8;
+constexpr float kSweepOn = 0.25f;
 
 // lanes per matrix
 template <int N>
@@ -517,7 +529,7 @@ struct Geometry {
     int64_t base;             // first item of this wave
     __device__ __forceinline__ Geometry(int64_t B) {
         lane = threadIdx.x & 63;
-        wave = threadIdx.x >> 6;
+        wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: base and the tile offsets go to SGPRs
         base = ((int64_t)blockIdx.x * kWaves + wave) * 64;
         const int64_t left = B * R - base;
         nvalid = __builtin_amdgcn_readfirstlane(left <= 0 ? 0 : left >= 64 ? 64 : (int)left);
@@ -845,17 +857,17 @@ __device__ __forceinline__ void newton_start(const Geometry<N, IO>& geo, uint4* 
     for (int j = 0; j < N; ++j) ok = ok && c[j] > 1.17549435e-38f;
     if (ok) {
         float q[M];   // product of the later sweeps' ratios
-#pragma unroll
-        for (int sw = 0; sw < kStartSweeps; ++sw) {
-            if (sw > 0) col_sums<N>(T, c);
+        // one sweep with c the column sums of T: scale the columns to sum to one and
+        // renormalise the rows; the first sweep sets y, later ones multiply into q
+        auto sweep = [&](bool first_sweep, bool second_sweep) __attribute__((always_inline)) {
             float rc[N];
 #pragma unroll
             for (int j = 0; j < N; ++j) rc[j] = rcp(c[j]);
 #pragma unroll
             for (int j = 0; j < M; ++j) {
                 const float ratio = c[N - 1] * rc[j];
-                if (sw == 0) y[j] = lg2(ratio);
-                else q[j] = (sw == 1) ? ratio : q[j] * ratio;
+                if (first_sweep) y[j] = lg2(ratio);
+                else q[j] = second_sweep ? ratio : q[j] * ratio;
             }
 #pragma unroll
             for (int i = 0; i < K; ++i) {
@@ -870,8 +882,22 @@ __device__ __forceinline__ void newton_start(const Geometry<N, IO>& geo, uint4* 
 #pragma unroll
                 for (int j = 0; j < N; ++j) T[i * N + j] *= r;
             }
+        };
+#pragma unroll
+        for (int sw = 0; sw < kStartSweeps; ++sw) {
+            if (sw > 0) col_sums<N>(T, c);
+            sweep(sw == 0, sw == 1);
         }
-        if constexpr (kStartSweeps > 1)
+        // the extra sweeps (q multiplies up to kStartSweeps + kMoreSweeps - 1 ratios
+        // in [n^-2, n^2]: at most 2^60 for n = 8, inside fp32's range); both lanes
+        // of a pair hold the same column sums and decide alike
+#pragma unroll 1
+        for (int sw = 0; sw < kMoreSweeps; ++sw) {
+            col_sums<N>(T, c);
+            if (!(col_residual<N>(c) > kSweepOn)) break;
+            sweep(false, kStartSweeps == 1 && sw == 0);
+        }
+        if constexpr (kStartSweeps + kMoreSweeps > 1)
 #pragma unroll
             for (int j = 0; j < M; ++j) y[j] += lg2(q[j]);
     }
@@ -1229,7 +1255,7 @@ implicit_bwd_from_T_kernel(const float* __restrict__ Tin, const float* __restric
 // read back.  Reads logits and dT, writes T, dual and dH.
 // ---------------------------------------------------------------------------
 template <int N, typename IO>
-__global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(N == 4 ? 6 : 3)))
+__global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(N == 4 ? 6 : 4)))
 fused_fwd_bwd_kernel(const IO* __restrict__ logits, const IO* __restrict__ dT, IO* __restrict__ Tout,
                      float* __restrict__ dual, IO* __restrict__ dH, int64_t B, float tol, int max_iter) {
     using Gm = Geometry<N, IO>;
