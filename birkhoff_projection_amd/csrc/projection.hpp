@@ -42,12 +42,14 @@ constexpr int kBlock = 256;  // threads per workgroup (4 waves of 64)
 // (residuals of a few 1e-2 after three sweeps) no lane takes the extra sweeps.
 // The decision is the lane's own, so a matrix's result does not depend on the
 // other matrices of the batch.
-// Measured on the hard-conditioning workload (sigma in {1, 3, 5, 8}): 84.6 us
-// with none, 72.9 with up to 3, 64.5 with up to 8, 65.4 with up to 12; the
-// moderate workloads are unchanged within 1 %.
+// Measured: the hard-conditioning forward (B = 2^20, sigma in {1, 3, 5, 8})
+// takes 84.6 us with no extra sweeps, 64.1 with these; the N(0, 10^2) forward at
+// B = 512 / 8192 / 131072 (latency-bound: its slowest lanes set the time) 56 /
+// 57 / 55 us before, 22 / 22 / 29 us with these; thresholds of 0.1 and 0.18 cost
+// the hard workload 5-15 %; moderate workloads are unchanged within 1 %.
 constexpr int kStartSweeps = 3;
-constexpr int kMoreSweeps = 8;
-constexpr float kSweepOn = 0.25f;
+constexpr int kMoreSweeps = 16;
+constexpr float kSweepOn = 0.4f;
 
 // lanes per matrix
 template <int N>
@@ -889,8 +891,9 @@ __device__ __forceinline__ void newton_start(const Geometry<N, IO>& geo, uint4* 
             sweep(sw == 0, sw == 1);
         }
         // the extra sweeps (q multiplies up to kStartSweeps + kMoreSweeps - 1 ratios
-        // in [n^-2, n^2]: at most 2^60 for n = 8, inside fp32's range); both lanes
+        // in [n^-2, n^2]: at most 2^108 for n = 8, inside fp32's range); both lanes
         // of a pair hold the same column sums and decide alike
+        static_assert((kStartSweeps + kMoreSweeps - 1) * 2 * (N == 8 ? 3 : 2) < 127, "q stays finite");
 #pragma unroll 1
         for (int sw = 0; sw < kMoreSweeps; ++sw) {
             col_sums<N>(T, c);

@@ -182,13 +182,13 @@ def test_parity_full_size_sampled(key):
     assert torch.isfinite(T.float()).all().item()
     idx = sample_indices(w.B)
     if stats is not None:
-        # the hard inputs take the fallback sweep (blog post, section 2.2) on some
-        # matrices: all of them join the sample
+        # matrices that take the fallback sweep (blog post, section 2.2) join the
+        # sample (the start's extra sweeps leave the hard inputs few or none; the
+        # underflow and large-span tests show the sweep at work)
         its, fbs = stats[0].cpu().numpy(), stats[1].cpu().numpy()
         assert (its >= 0).all() and ((fbs >= 0) & (fbs <= its)).all()
         took = np.flatnonzero(fbs > 0)
-        assert took.size > 0, "no matrix took the fallback sweep"
-        print("  %d matrices took %d fallback sweeps" % (took.size, fbs.sum()))
+        print("  %d matrices took %d fallback sweeps, max updates %d" % (took.size, fbs.sum(), its.max()))
         idx = np.unique(np.concatenate([idx, took[:4096]]))
     it = torch.from_numpy(idx).to(DEV)
     H64 = W.decode_f64(Hs[idx])
@@ -759,8 +759,9 @@ def test_parity_pages_timing_shape(B):
     benchmark workload) through the forward (gathering kernel), the backward and the
     one-launch forward + backward, against the oracle.  Many of these projections are
     nearly permutations, where eq (13) is ill-conditioned; the backward is checked
-    by backward_check.  Some matrices take the fallback sweep (blog post, section
-    2.2); the counts say which, and they meet the gates like the rest."""
+    by backward_check.  Matrices that take the fallback sweep (blog post, section
+    2.2) meet the gates like the rest; the start's extra sweeps leave these inputs
+    few or none (the underflow and large-span tests show the sweep at work)."""
     w = W.pages_shape_workload(B)
     print("case pages shape", B, flush=True)
     Hs = W.make_logits(w)
@@ -775,7 +776,6 @@ def test_parity_pages_timing_shape(B):
     it, fbn = iters.cpu().numpy(), fb.cpu().numpy()
     assert (it >= 0).all(), (it < 0).sum()
     assert ((fbn >= 0) & (fbn <= it)).all()
-    assert (fbn > 0).any(), "no matrix took the fallback sweep"
     assert torch.equal(T, T2) and torch.equal(dual, dual2)
     T_ref, _, st = oracle.project(H64, sk_cap=w.sk_cap)
     assert (st >= 0).all()
@@ -785,10 +785,10 @@ def test_parity_pages_timing_shape(B):
     loose, r1 = backward_check(host_f64(dH), rebuilt_T(H64, dg), G64, T_ref, "bwd")
     _, r2 = backward_check(host_f64(dH2), Tg, G64, T_ref, "fused")
     _, r3 = backward_check(host_f64(dH3), Tg, G64, T_ref, "from_T")
+    fb_err = np.abs(Tg - T_ref)[fbn > 0].max() if (fbn > 0).any() else 0.0
     print("  max updates %d, %d matrices took %d fallback sweeps; fwd err %.2e (fallback matrices %.2e), "
           "residual %.2e; bwd worst error/gate %.2f / %.2f / %.2f, %d of %d with a loose gate" % (
-              it.max(), (fbn > 0).sum(), fbn.sum(), err, np.abs(Tg - T_ref)[fbn > 0].max(), res, r1, r2, r3,
-              loose, B))
+              it.max(), (fbn > 0).sum(), fbn.sum(), err, fb_err, res, r1, r2, r3, loose, B))
 
 
 @pytest.mark.parametrize("B", [1, 65, 257, 1000, 1320])
@@ -1149,9 +1149,13 @@ def test_underflowed_start_is_verified(n, depth):
     _, _, T2, dual2, dH = run_fused(w, Hs, G32)
     torch.cuda.synchronize()
     assert torch.equal(T, T2) and torch.equal(dual, dual2) and torch.equal(T, T3) and torch.equal(dual, dual3)
-    it = iters.cpu().numpy()
+    it, fbn = iters.cpu().numpy(), fb.cpu().numpy()
     assert (it >= 0).all(), (it < 0).sum()
-    print("  updates: mean %.1f max %d, fallback sweeps max %d" % (it.mean(), it.max(), fb.cpu().numpy().max()))
+    assert ((fbn >= 0) & (fbn <= it)).all()
+    # the shared column keeps every step size from being accepted: these
+    # matrices converge through fallback sweeps, and meet the gates below
+    assert (fbn > 0).mean() >= 0.5, (fbn > 0).mean()
+    print("  updates: mean %.1f max %d, fallback sweeps max %d" % (it.mean(), it.max(), fbn.max()))
     H64 = Hs.astype(np.float64)
     T_ref, _, st = oracle.project(H64, sk_cap=5_000)
     assert (st >= 0).all()
