@@ -1006,8 +1006,10 @@ struct Gather {
     static constexpr int kRegion = G::Tile::kLdsChunks > kRecordChunks ? G::Tile::kLdsChunks : kRecordChunks;
 };
 
-// (the statistics variant, which also carries the counts, at six waves per SIMD
-// so that it does not spill)
+// The dual of every matrix of the workgroup is collected in LDS and written out
+// as one contiguous block by the wave that finishes last (an LDS counter says
+// which): a gathered lane's 16-byte dual alone would be a partial write to HBM,
+// and so would the fast lanes' around it.
 template <typename IO, bool kStats>
 __global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kStats ? 6 : 7)))
 newton_fwd_gather_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, float* __restrict__ dual,
@@ -1017,12 +1019,20 @@ newton_fwd_gather_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, f
     constexpr int N = Q::N, M = Q::M, KN = Q::KN;
     using G = typename Q::G;
     __shared__ uint4 lds[kWaves][Q::kRegion];
-    __shared__ int handed[kWaves];   // states a wave handed off; -1: it keeps its slow lanes
+    __shared__ uint4 duals[kBlock];   // the workgroup's duals, by matrix
+    __shared__ int handed[kWaves];    // states a wave handed off; -1: it keeps its slow lanes
+    __shared__ int finished;          // waves done with their matrices
     const G geo(B);
     const int first = max_iter < kFirstPass ? max_iter : kFirstPass;
     float T[KN], y[M], c[N], res = 0.0f;
     int it = 0, sweeps = 0;
     bool slow = false, wide = false, checked = false;
+    // the lane's dual, base-e with beta_{N-1} = 0, into the workgroup's block
+    auto keep_dual = [&](int slot) __attribute__((always_inline)) {
+        duals[slot] = make_uint4(__float_as_uint(y[0] * kLn2), __float_as_uint(y[1] * kLn2),
+                                 __float_as_uint(y[2] * kLn2), 0u);
+    };
+    if (threadIdx.x == 0) finished = 0;
     if (geo.nvalid > 0) {   // wave-uniform; waves past the end still reach the barrier
         newton_start<N, IO>(geo, lds[geo.wave], logits, T, y, c, res, wide);
         newton_iterate<N, IO, false>(logits, WaveItem{geo.base}, tol, first, T, y, c, res, it, wide, checked, sweeps);
@@ -1034,11 +1044,7 @@ newton_fwd_gather_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, f
             G::Tile::store_except(w, lds[geo.wave], geo.lane, geo.chunks(Tout), geo.nvalid * G::C, mask);
         }
         if (geo.valid() && !slow) {
-            float beta[N];
-#pragma unroll
-            for (int j = 0; j < M; ++j) beta[j] = y[j] * kLn2;
-            beta[M] = 0.0f;
-            store_dual<N>(dual, geo.matrix(), 0, beta);
+            keep_dual(threadIdx.x);
             if (kStats) {
                 iters[geo.matrix()] = (res <= tol) ? it : -1;
                 if (fallbacks) fallbacks[geo.matrix()] = sweeps;
@@ -1076,12 +1082,11 @@ newton_fwd_gather_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, f
         total += h > 0 ? h : 0;
         rank += (v < geo.wave && h >= 0) ? 1 : 0;
     }
-    int64_t item = geo.item();
-    if (handed[geo.wave] >= 0) {
-        // a taking wave: handed-off state number t = rank * 64 + lane, if it exists
-        // (the takers are at least half as many as the waves that handed off, each of
-        // which handed off at most kHandOff <= 32 states, so all are taken)
-        if (rank * 64 >= total) return;
+    int slot = threadIdx.x;   // the lane's matrix in the workgroup
+    // a taking wave: handed-off state number t = rank * 64 + lane, if it exists
+    // (the takers are at least half as many as the waves that handed off, each of
+    // which handed off at most kHandOff <= 32 states, so all are taken)
+    if (handed[geo.wave] >= 0 && rank * 64 < total) {
         const int t = rank * 64 + geo.lane;
         slow = t < total;
         if (slow) {
@@ -1101,7 +1106,7 @@ newton_fwd_gather_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, f
 #pragma unroll
             for (int j = 0; j < N; ++j) c[j] = rec[(KN + M + j) * kHandOff + p];
             const int word = __float_as_int(rec[(KN + M + N) * kHandOff + p]);
-            item = (int64_t)blockIdx.x * kBlock + (word & 0xFF);
+            slot = word & 0xFF;
             wide = (word & 0x100) != 0;
             checked = (word & 0x200) != 0;
             sweeps = word >> 10;
@@ -1110,20 +1115,33 @@ newton_fwd_gather_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, f
         }
     }
     if (slow) {
+        const int64_t item = (int64_t)blockIdx.x * kBlock + slot;
         newton_iterate<N, IO, false>(logits, LaneItem{item}, tol, max_iter, T, y, c, res, it, wide, checked, sweeps);
         uint4 w[G::C];
         Storage<IO>::template encode<KN>(T, w);
+        // cached stores: the L2 merges these scattered 64-byte pieces with the
+        // lines around them (streaming stores of them cost 4 % more HBM writes)
         uint4* q = reinterpret_cast<uint4*>(Tout) + item * G::C;
 #pragma unroll
-        for (int k = 0; k < G::C; ++k) stream_store(q + k, w[k]);
-        float beta[N];
-#pragma unroll
-        for (int j = 0; j < M; ++j) beta[j] = y[j] * kLn2;
-        beta[M] = 0.0f;
-        store_dual<N>(dual, item, 0, beta);
+        for (int k = 0; k < G::C; ++k) q[k] = w[k];
+        keep_dual(slot);
         if (kStats) {
             iters[item] = (res <= tol) ? it : -1;
             if (fallbacks) fallbacks[item] = sweeps;
+        }
+    }
+    // the last wave to finish writes the workgroup's duals (its valid matrices)
+    int before = 0;
+    if (geo.lane == 0) before = __hip_atomic_fetch_add(&finished, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+    before = __shfl(before, 0);
+    if (before == kWaves - 1) {
+        const int64_t left = B - (int64_t)blockIdx.x * kBlock;
+        const int valid = left >= kBlock ? kBlock : (int)left;
+        uint4* q = reinterpret_cast<uint4*>(dual) + (int64_t)blockIdx.x * kBlock;
+#pragma unroll
+        for (int k = 0; k < kBlock / 64; ++k) {
+            const int m = k * 64 + geo.lane;
+            if (m < valid) stream_store(q + m, duals[m]);
         }
     }
 }

@@ -54,11 +54,18 @@ def kernels(asm):
 
 
 def test_all_global_stores_are_non_temporal(asm):
+    """Streaming stores everywhere, but for the gathering forward's per-lane T of a
+    gathered matrix (one 64-byte fp32 or 32-byte bf16 piece among lines written
+    by other waves), which is cached so that the L2 merges it (4 or 2 stores)."""
     ks = kernels(asm)
     assert ks
     for name, (body, *_rest) in ks.items():
-        for line in re.findall(r"^\s+global_store_dwordx4.*$", body, flags=re.M):
-            assert line.rstrip().endswith(" nt"), (name, line)
+        cached = [line for line in re.findall(r"^\s+global_store_dwordx4.*$", body, flags=re.M)
+                  if not line.rstrip().endswith(" nt")]
+        if "newton_fwd_gather_kernel" in name:
+            assert len(cached) == (4 if "gather_kernelIf" in name else 2), (name, cached)
+        else:
+            assert not cached, (name, cached)
 
 
 def test_n4_kernels_occupancy_and_no_spills(asm):
