@@ -139,11 +139,23 @@ def timed_steps(fn, sets, K: int, stream, probe=None) -> float:
     return e0.elapsed_time(e1) / K
 
 
+def per_kernel_time(fn, sets, K: int, stream, settle_ms: float, probe, clocks: dict, name: str) -> float:
+    """A per-kernel figure: `fn` alone, back to back for a quarter of the settle
+    time (at least 20 ms) so that the engine clock settles on that kernel's own
+    load, then K timed launches (timed_steps); the clock after them goes into
+    clocks[name].  Returns ms per launch."""
+    settle(fn, sets, max(20.0, settle_ms / 4))
+    ms = timed_steps(fn, sets, K, stream, probe)
+    clocks[name] = round(probe.mhz(), 1)
+    return ms
+
+
 def clock_report(settle_steps, settle_ms, probe):
     """The settle phase and the engine clock measured right after the timed region
     (shader-clock cycles per constant-rate tick, birkhoff_clock_probe)."""
     return {"settle_ms": settle_ms, "settle_steps": settle_steps,
-            "mhz_after_timed_region": round(probe.mhz(), 1), "peak_mhz": CLOCK_HZ / 1e6}
+            "mhz_after_timed_region": round(probe.mhz(), 1), "peak_mhz": CLOCK_HZ / 1e6,
+            "mhz_after_per_kernel": {}}
 
 
 def cpu_model() -> str:
@@ -297,6 +309,9 @@ def eot_report(w, args, dev):
     def timed(fn, K, probe=None):
         return timed_steps(fn, sets, K, stream, probe)
 
+    def kernel_time(fn, name):
+        return per_kernel_time(fn, sets, args.steps, stream, args.settle_ms, probe, clock["mhz_after_per_kernel"], name)
+
     settle_steps = settle(step, sets, args.settle_ms)
     probe = bp.ClockProbe(dev)
     for i in range(args.warmup):
@@ -305,8 +320,8 @@ def eot_report(w, args, dev):
     K = args.steps
     ms_step = timed(step, K, probe)
     clock = clock_report(settle_steps, args.settle_ms, probe)
-    fwd_ms = timed(run_fwd, K)
-    bwd_ms = timed(run_bwd, K)
+    fwd_ms = kernel_time(run_fwd, "birkhoff_eot_fwd")
+    bwd_ms = kernel_time(run_bwd, "birkhoff_eot_bwd")
     iters = torch.empty(B, dtype=torch.int32, device=dev)
     st = sets[0]
     bp.birkhoff_eot_fwd(st["M"], st["a"], st["b"], st["T"], st["dual"], iters, w.eta, w.tol, w.max_iter, stream)
@@ -410,6 +425,9 @@ def mix_report(w, args, dev):
     def timed(fn, K, probe=None):
         return timed_steps(fn, sets, K, stream, probe)
 
+    def kernel_time(fn, name):
+        return per_kernel_time(fn, sets, args.steps, stream, args.settle_ms, probe, clock["mhz_after_per_kernel"], name)
+
     settle_steps = settle(step, sets, args.settle_ms)
     probe = bp.ClockProbe(dev)
     for i in range(args.warmup):
@@ -418,8 +436,8 @@ def mix_report(w, args, dev):
     K = args.steps
     ms_step = timed(step, K, probe)
     clock = clock_report(settle_steps, args.settle_ms, probe)
-    fwd_ms = timed(run_fwd, K)
-    bwd_ms = timed(run_bwd, K)
+    fwd_ms = kernel_time(run_fwd, "birkhoff_fwd_mix")
+    bwd_ms = kernel_time(run_bwd, "birkhoff_mix_bwd")
     # context only: the same product through torch's batched matmul on the stored T
     def run_torch(s):
         torch.matmul(s["T"].to(s["x"].dtype), s["x"], out=s["y"])
@@ -480,6 +498,9 @@ def forward_only_report(w, args, dev):
     def timed(fn, K, probe=None):
         return timed_steps(fn, sets, K, stream, probe)
 
+    def kernel_time(fn, name):
+        return per_kernel_time(fn, sets, args.steps, stream, args.settle_ms, probe, clock["mhz_after_per_kernel"], name)
+
     settle_steps = settle(run_fwd, sets, args.settle_ms)
     probe = bp.ClockProbe(dev)
     for i in range(args.warmup):
@@ -487,7 +508,7 @@ def forward_only_report(w, args, dev):
     K = args.steps
     ms = timed(run_fwd, K, probe)
     clock = clock_report(settle_steps, args.settle_ms, probe)
-    ms_sk = timed(run_sk, K)
+    ms_sk = kernel_time(run_sk, "sinkhorn_fwd")
     st = sets[0]
     iters = torch.empty(B, dtype=torch.int32, device=dev)
     bp.birkhoff_fwd_ex(st["H"], st["T"], st["dual"], iters, w.tol, w.max_iter, stream)
@@ -780,6 +801,9 @@ def forward_backward_report(w, args, dev):
     def timed(fn, K, probe=None):
         return timed_steps(fn, sets, K, stream, probe)
 
+    def kernel_time(fn, name):
+        return per_kernel_time(fn, sets, args.steps, stream, args.settle_ms, probe, clock["mhz_after_per_kernel"], name)
+
     settle_steps = settle(step, sets, args.settle_ms)
     probe = bp.ClockProbe(dev)
     for i in range(args.warmup):
@@ -790,13 +814,14 @@ def forward_backward_report(w, args, dev):
     ms_step = timed(step, K, probe)      # the timed region: K whole steps
     clock = clock_report(settle_steps, args.settle_ms, probe)
     other = step_separate if args.path == "fused" else run_fused
-    ms_other = timed(other, K)           # the other form of the step, for comparison
-    fwd_ms = timed(run_fwd, K)           # per-kernel launch times, same stream
-    bwd_ms = timed(run_bwd, K)
+    ms_other = kernel_time(other, "other_path")   # the other form of the step, for comparison
+    fwd_ms = kernel_time(run_fwd, "birkhoff_fwd")  # per-kernel launch times, same stream
+    bwd_ms = kernel_time(run_bwd, "birkhoff_bwd")
     fused_ms = ms_step if args.path == "fused" else ms_other
     bwd_t_ms = None
     if w.io == "f32":                    # the backward from T alone (what autograd uses for fp32)
-        bwd_t_ms = timed(lambda s: bp.birkhoff_bwd_from_T(s["T"], s["G"], s["dH"], stream), K)
+        bwd_t_ms = kernel_time(lambda s: bp.birkhoff_bwd_from_T(s["T"], s["G"], s["dH"], stream),
+                               "birkhoff_bwd_from_T")
 
     def step_on_current(s):   # the same step, launched on whatever stream is current
         if args.path == "fused":
