@@ -255,9 +255,13 @@ struct WaveTile {
         }
     }
 
-    // Waits for a prefetch and hands each lane its own C chunks.
+    // Waits for a prefetch and hands each lane its own C chunks.  kPin: the
+    // addresses are recomputed from the lane here (opaque) instead of being kept
+    // from the load, which kernels near their register limit need; others spend
+    // fewer instructions without it.
+    template <bool kPin = true>
     __device__ __forceinline__ static void read_prefetched(uint4* lds, int lane, uint4 (&own)[C]) {
-        lane = opaque(lane);
+        if constexpr (kPin) lane = opaque(lane);
         __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0): the LDS copies have landed
         wave_lds_sync();
 #pragma unroll
@@ -267,10 +271,11 @@ struct WaveTile {
 
     // As store, but the items whose bit is set in the wave-uniform mask `skip`
     // (bit m = the wave's m-th item) are not written.
+    template <bool kPin = true>
     __device__ __forceinline__ static void store_except(const uint4 (&own)[C], uint4* lds, int lane,
                                                         uint4* __restrict__ dst, int valid, uint64_t skip) {
         static_assert(kStaged, "staged tiles only");
-        lane = opaque(lane);
+        if constexpr (kPin) lane = opaque(lane);
 #pragma unroll
         for (int q = 0; q < C; ++q) lds[slot(lane, q)] = own[q];
         wave_lds_sync();
@@ -285,9 +290,11 @@ struct WaveTile {
 
     // Registers of the owning lane -> global.  `valid` (wave-uniform) chunks
     // exist; the rest are not written.  A full tile stores unconditionally.
+    // (kPin as in read_prefetched.)
+    template <bool kPin = true>
     __device__ __forceinline__ static void store(const uint4 (&own)[C], uint4* lds, int lane, uint4* __restrict__ dst,
                                                  int valid) {
-        lane = opaque(lane);
+        if constexpr (kPin) lane = opaque(lane);
         const bool full = valid == 64 * C;
         if constexpr (kStaged) {
 #pragma unroll
