@@ -99,7 +99,15 @@ def check_forward(w, H64, T_gpu, dual_gpu, T_ref):
     err = np.abs(T_gpu - T_ref)
     if w.io == "bf16":
         assert (err <= FWD_TOL + half_ulp_bf16(T_ref)).all(), err.max()
-        res = residual(rebuilt_T(H64, dual_gpu)).max()
+        # T rebuilt in float64 from the stored fp32 dual: the dual's own rounding,
+        # |beta_j| 2^-24 per entry, moves a column sum by up to about twice its
+        # largest (the Hessian's rows have absolute sums of at most 2); four times
+        # that is allowed on top of the gate (1e-6 at the benchmark's |beta| ~ 4,
+        # 1e-5 at the |beta| ~ 40 of N(0, 10^2) logits)
+        r = residual(rebuilt_T(H64, dual_gpu))
+        slack = 4.0 * np.abs(dual_gpu).max(axis=1) * U32
+        assert (r <= RES_TOL + slack).all(), (r.max(), (r / (RES_TOL + slack)).max())
+        res = r.max()
     else:
         assert err.max() <= FWD_TOL, err.max()
         res = residual(T_gpu).max()
@@ -974,10 +982,9 @@ def test_distribution_sweep(kind, n, io):
     oracle: forward and residual gates as everywhere, the backward by
     backward_check (bf16: its part (a), with half an ulp for the stored rounding),
     and the forward-only launch equal to the one-launch forward bit for bit.
-    bf16 storage stops at scale 8: at N(0, 10^2) the fp32 dual, |beta| ~ 30, is
-    itself rounded by ~2e-6, so T rebuilt from it misses the 1e-5 residual gate."""
-    if io == "bf16" and kind == "normal:10":
-        pytest.skip("outside the bf16 reading's residual gate (see docstring)")
+    In bf16 storage the residual is that of T rebuilt from the stored fp32 dual,
+    whose own rounding at the |beta| ~ 40 of N(0, 10^2) logits check_forward
+    allows for."""
     rng = np.random.default_rng([n, SWEEP_KINDS.index(kind), int(io == "bf16")])
     B = 3000 + 17 * n
     print("case sweep %s n=%d %s" % (kind, n, io), flush=True)
@@ -1264,3 +1271,17 @@ def test_double_backward_raises():
     (g,) = torch.autograd.grad((T * T).sum(), H, create_graph=True)
     with pytest.raises(RuntimeError):
         g.sum().backward()
+    # the general plan (uniform marginals of mass one) and the fused mixing
+    cost = torch.randn((64, 4, 6), device=DEV, requires_grad=True)
+    a = torch.full((64, 4), 0.25, device=DEV)
+    b = torch.full((64, 6), 1.0 / 6.0, device=DEV)
+    P = bp.EntropicOT.apply(cost, a, b, 1.0)
+    (g,) = torch.autograd.grad((P * P).sum(), cost, create_graph=True)
+    with pytest.raises(RuntimeError):
+        g.sum().backward()
+    Hm = torch.randn((8, 4, 4), device=DEV, requires_grad=True)
+    x = torch.randn((8, 4, 64), device=DEV, requires_grad=True)
+    y = bp.ProjectMix.apply(Hm, x)
+    gH, gx = torch.autograd.grad((y * y).sum(), (Hm, x), create_graph=True)
+    with pytest.raises(RuntimeError):
+        (gH.sum() + gx.sum()).backward()
