@@ -5,7 +5,7 @@
 // token's n x C hidden matrix (n = 4 streams of C features).
 //
 // Forward (project_mix_kernel): a workgroup takes 4 tokens, one per wave.  Its first wave
-// projects their logits exactly as newton_fwd_kernel does (one matrix per
+// projects their logits exactly as birkhoff_fwd does (one matrix per
 // lane) and stores T and the dual; the 4 projections go to LDS, and then all
 // four waves stream the tokens' hidden matrices, one token each, through
 // y_i = sum_j T_ij x_j (each wave's first loads are issued before the

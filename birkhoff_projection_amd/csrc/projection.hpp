@@ -988,7 +988,8 @@ newton_fwd_kernel(const IO* __restrict__ logits, IO* __restrict__ Tout, float* _
 // off (or had nothing left) take the handed-off states 64 to a wave and carry
 // them on to tol or max_iter, while the rest exit, so that the updates of the
 // tail are spent on fewer waves.  Every matrix goes through exactly the updates
-// of newton_fwd_kernel from the same state, so the results are bit-identical.
+// of the fused kernel's forward from the same state (the loop shapes differ, the
+// arithmetic of each update does not), so T and the dual are bit-identical.
 // ---------------------------------------------------------------------------
 constexpr int kFirstPass = 4;   // updates before the slow lanes are gathered
 constexpr int kHandOff = 32;    // most slow lanes a wave hands to the workgroup
@@ -1274,7 +1275,7 @@ implicit_bwd_from_T_kernel(const float* __restrict__ Tin, const float* __restric
 
 // ---------------------------------------------------------------------------
 // Forward and backward in one launch, for callers that hold dL/dT when they
-// project.  The forward is newton_fwd_kernel's; the backward is eq (13) at the
+// project.  The forward is newton_solve, as in birkhoff_fwd; the backward is eq (13) at the
 // final iterate T, still in registers, so neither the logits nor the dual are
 // read back.  Reads logits and dT, writes T, dual and dH.
 // ---------------------------------------------------------------------------
