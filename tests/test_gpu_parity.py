@@ -1262,6 +1262,42 @@ def test_backward_deflated_block(n):
     print("  block error/gate %.2f" % (np.abs(host_f64(dH)[:, 1:, 1:] - dHs).max(axis=(1, 2)) / gate).max())
 
 
+@pytest.mark.parametrize("n", [4, 8])
+def test_results_do_not_depend_on_the_batch(n):
+    """A matrix's T and dual do not depend on the other matrices of the batch or
+    on its position in it: the start's extra sweeps and the convergence check are
+    each lane's own decisions, and a gathered matrix goes through the same updates
+    wherever it is carried on.  Logits of mixed scales (N(0, s^2), s from 0.5 to
+    12) are projected as one batch, in reverse order, and in sub-batches of 1, 63
+    and 200; every result must equal the first bit for bit (gathering forward and
+    fused kernel alike)."""
+    rng = np.random.default_rng([n, 77])
+    B = 1000
+    scales = rng.choice([0.5, 1.0, 3.0, 8.0, 12.0], size=B)
+    H32 = (scales[:, None, None] * rng.standard_normal((B, n, n))).astype(np.float32)
+    G32 = rng.standard_normal((B, n, n)).astype(np.float32)
+    w = W.Workload(key="batch", title="", B=B, n=n, io="f32", logits=None, upstream=None, passes="fwd+bwd",
+                   seed=0, max_iter=100)
+    print("case batch independence n=%d" % n, flush=True)
+    _, T, dual, _ = run_fwd(w, H32)
+    _, _, T2, dual2, _ = run_fused(w, H32, G32)
+    torch.cuda.synchronize()
+    assert torch.equal(T, T2) and torch.equal(dual, dual2)
+    Tn, dn = T.cpu().numpy(), dual.cpu().numpy()
+    rev = np.arange(B)[::-1]
+    _, Tr, dr, _ = run_fwd(w, H32[rev])
+    torch.cuda.synchronize()
+    assert np.array_equal(Tr.cpu().numpy(), Tn[rev]) and np.array_equal(dr.cpu().numpy(), dn[rev])
+    for lo, hi in ((137, 138), (500, 563), (800, 1000)):
+        _, Ts, ds, _ = run_fwd(w, H32[lo:hi])
+        _, _, Tf, df, _ = run_fused(w, H32[lo:hi], G32[lo:hi])
+        torch.cuda.synchronize()
+        for X, Y in ((Ts, T), (Tf, T)):
+            assert np.array_equal(X.cpu().numpy(), Y.cpu().numpy()[lo:hi]), (lo, hi)
+        for X in (ds, df):
+            assert np.array_equal(X.cpu().numpy(), dn[lo:hi]), (lo, hi)
+
+
 def test_double_backward_raises():
     """The autograd functions' backward passes are computed by the kernels, not
     from differentiable torch operations, so a second derivative through them is
