@@ -188,7 +188,8 @@ print(json.dumps({"seconds": time.perf_counter() - t0, "threads": oracle.threads
 
 def one_core_baseline(w, per_matrix_s: float, target_s: float = 5.0):
     """The same oracle on one core: a child process with OMP_NUM_THREADS=1 on a
-    prefix sized from the all-core rate to about target_s seconds."""
+    prefix sized to about target_s seconds from per_matrix_s, the one-core time
+    per matrix that the all-core run implies."""
     import os
     import subprocess
     Bs = int(min(w.B, max(256, target_s / max(per_matrix_s, 1e-9))))
@@ -245,7 +246,7 @@ def cpu_baseline(w, target_s: float = 10.0):
                       % (Bs, "all of it" if Bs == w.B else "a prefix", w.sk_cap,
                          "" if fwd_only else ", then the eq (13) backward", dt),
             "cpu_model": cpu_model(), "parts": parts,
-            "one_core": one_core_baseline(w, dt / Bs)}
+            "one_core": one_core_baseline(w, dt / Bs * oracle.threads())}
 
 
 def eot_cpu_baseline(w, target_s: float = 10.0):
