@@ -169,38 +169,68 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
+def oracle_seconds(kind: str, key: str, Bs: int) -> float:
+    """Wall time of the float64 oracle on the first Bs items of a workload, on the
+    threads OpenMP gives it: "proj" the certified projection and, where the
+    workload has an upstream gradient, the eq (13) backward; "eot" the certified
+    general plan and its backward; "mix" the projection, y = T x, its backward and
+    eq (13)."""
+    import oracle
+    from birkhoff_projection_amd import workloads as W
+    if kind == "proj":
+        w = W.WORKLOADS[key]
+        H = W.decode_f64(W.make_logits(w, B=Bs))
+        G = None if w.upstream is None else W.decode_f64(W.make_upstream(w, B=Bs))
+        t0 = time.perf_counter()
+        T, _, _ = oracle.project(H, sk_cap=w.sk_cap)
+        if G is not None:
+            oracle.bwd(T, G)
+        return time.perf_counter() - t0
+    if kind == "eot":
+        w = W.EOT_WORKLOADS[key]
+        M, a, b = W.make_eot(w, B=Bs)
+        G = W.make_eot_upstream(w, B=Bs)
+        M, a, b, G = (x.astype("float64") for x in (M, a, b, G))
+        t0 = time.perf_counter()
+        T, _, _ = oracle.eot_project(M, a, b, w.eta, sk_cap=w.sk_cap)
+        oracle.eot_bwd(T, G, a, b, w.eta)
+        return time.perf_counter() - t0
+    w = W.MIX_WORKLOADS[key]
+    H, x, dy = W.make_mix(w, B=Bs)
+    H, x, dy = H.astype("float64"), W.decode_f64(x), W.decode_f64(dy)
+    t0 = time.perf_counter()
+    T, _, _ = oracle.project(H)
+    oracle.mix(T, x)
+    _, dT = oracle.mix_bwd(T, x, dy)
+    oracle.bwd(T, dT)
+    return time.perf_counter() - t0
+
+
 ONE_CORE_SCRIPT = r"""
-import json, sys, time
+import json, sys
 sys.path.insert(0, sys.argv[1])
-import oracle
-from birkhoff_projection_amd import workloads as W
-w = W.WORKLOADS[sys.argv[2]]
-B = int(sys.argv[3])
-H = W.decode_f64(W.make_logits(w, B=B))
-G = None if w.upstream is None else W.decode_f64(W.make_upstream(w, B=B))
-t0 = time.perf_counter()
-T, _, _ = oracle.project(H, sk_cap=w.sk_cap)
-if G is not None:
-    oracle.bwd(T, G)
-print(json.dumps({"seconds": time.perf_counter() - t0, "threads": oracle.threads()}))
+import bench, oracle
+print(json.dumps({"seconds": bench.oracle_seconds(sys.argv[2], sys.argv[3], int(sys.argv[4])),
+                  "threads": oracle.threads()}))
 """
 
 
-def one_core_baseline(w, per_matrix_s: float, target_s: float = 5.0):
+def one_core_baseline(kind: str, key: str, n_items: int, per_item_s: float, unit: str = "matrices",
+                      target_s: float = 5.0):
     """The same oracle on one core: a child process with OMP_NUM_THREADS=1 on a
-    prefix sized to about target_s seconds from per_matrix_s, the one-core time
-    per matrix that the all-core run implies."""
+    prefix sized to about target_s seconds from per_item_s, the one-core time
+    per item that the all-core run implies."""
     import os
     import subprocess
-    Bs = int(min(w.B, max(256, target_s / max(per_matrix_s, 1e-9))))
+    Bs = int(min(n_items, max(256, target_s / max(per_item_s, 1e-9))))
     env = dict(os.environ, OMP_NUM_THREADS="1")
-    r = subprocess.run([sys.executable, "-c", ONE_CORE_SCRIPT, str(ROOT), w.key, str(Bs)], env=env,
+    r = subprocess.run([sys.executable, "-c", ONE_CORE_SCRIPT, str(ROOT), kind, key, str(Bs)], env=env,
                        capture_output=True, text=True, timeout=300)
     if r.returncode != 0:
         return {"error": r.stderr.strip().splitlines()[-1] if r.stderr.strip() else "failed"}
     d = json.loads(r.stdout.strip().splitlines()[-1])
     return {"value": Bs / d["seconds"], "cores": d["threads"],
-            "sample": "the first %d matrices, %.1f s wall" % (Bs, d["seconds"])}
+            "sample": "the first %d %s, %.1f s wall" % (Bs, unit, d["seconds"])}
 
 
 def cpu_baseline(w, target_s: float = 10.0):
@@ -246,7 +276,7 @@ def cpu_baseline(w, target_s: float = 10.0):
                       % (Bs, "all of it" if Bs == w.B else "a prefix", w.sk_cap,
                          "" if fwd_only else ", then the eq (13) backward", dt),
             "cpu_model": cpu_model(), "parts": parts,
-            "one_core": one_core_baseline(w, dt / Bs * oracle.threads())}
+            "one_core": one_core_baseline("proj", w.key, w.B, dt / Bs * oracle.threads())}
 
 
 def eot_cpu_baseline(w, target_s: float = 10.0):
@@ -255,23 +285,16 @@ def eot_cpu_baseline(w, target_s: float = 10.0):
     import oracle
     from birkhoff_projection_amd import workloads as W
 
-    def run(Bs):
-        M, a, b = W.make_eot(w, B=Bs)
-        G = W.make_eot_upstream(w, B=Bs)
-        M, a, b, G = (x.astype("float64") for x in (M, a, b, G))
-        t0 = time.perf_counter()
-        T, _, _ = oracle.eot_project(M, a, b, w.eta, sk_cap=w.sk_cap)
-        oracle.eot_bwd(T, G, a, b, w.eta)
-        return time.perf_counter() - t0
-
     probe = 8192
-    dt = run(probe)
+    dt = oracle_seconds("eot", w.key, probe)
     Bs = int(min(w.B, max(probe, probe * target_s / max(dt, 1e-6))))
-    dt = run(Bs)
+    dt = oracle_seconds("eot", w.key, Bs)
     return {"value": Bs / dt, "unit": "problems/s", "cores": oracle.threads(), "kind": "oracle",
             "sample": "the first %d problems of the same seeded workload (%s), float64: Sinkhorn to 1e-13 "
                       "with a Newton cross-check, then the eq (13) backward; %.1f s wall"
-                      % (Bs, "all of it" if Bs == w.B else "a prefix", dt)}
+                      % (Bs, "all of it" if Bs == w.B else "a prefix", dt),
+            "cpu_model": cpu_model(),
+            "one_core": one_core_baseline("eot", w.key, w.B, dt / Bs * oracle.threads(), "problems")}
 
 
 def eot_report(w, args, dev):
@@ -361,24 +384,16 @@ def mix_cpu_baseline(w, target_s: float = 10.0):
     import oracle
     from birkhoff_projection_amd import workloads as W
 
-    def run(Bs):
-        H, x, dy = W.make_mix(w, B=Bs)
-        H, x, dy = H.astype("float64"), W.decode_f64(x), W.decode_f64(dy)
-        t0 = time.perf_counter()
-        T, _, _ = oracle.project(H)
-        oracle.mix(T, x)
-        _, dT = oracle.mix_bwd(T, x, dy)
-        oracle.bwd(T, dT)
-        return time.perf_counter() - t0
-
     probe = 256
-    dt = run(probe)
+    dt = oracle_seconds("mix", w.key, probe)
     Bs = int(min(w.B, max(probe, probe * target_s / max(dt, 1e-6))))
-    dt = run(Bs)
+    dt = oracle_seconds("mix", w.key, Bs)
     return {"value": Bs / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
             "sample": "the first %d tokens of the same seeded workload (%s), float64: the certified projection, "
                       "y = T x, dx = T^T dy, dT = dy x^T and the eq (13) backward; %.1f s wall"
-                      % (Bs, "all of it" if Bs == w.B else "a prefix", dt)}
+                      % (Bs, "all of it" if Bs == w.B else "a prefix", dt),
+            "cpu_model": cpu_model(),
+            "one_core": one_core_baseline("mix", w.key, w.B, dt / Bs * oracle.threads(), "tokens")}
 
 
 def mix_report(w, args, dev):
