@@ -35,11 +35,14 @@
  *     error: its last iterate is written (see birkhoff_fwd_ex to detect it).
  *     Non-finite logits yield NaN in that matrix's outputs only.
  *   - The backward passes solve eq (13)'s system with Delta, the Hessian at
- *     the projection.  Where Delta is numerically singular (a projection within
- *     rounding of a permutation on some rows and columns), dH does not depend
- *     on the undetermined part of the solution; the system is then solved
- *     rescaled and with a shift of 2^-22 of its trace, and at an exact
- *     permutation (Delta = 0) the result is the exact dH = 0.
+ *     the projection, by Cholesky.  Where Delta is numerically singular (a
+ *     projection within rounding of a permutation on some rows and columns), dH
+ *     does not depend on the undetermined part of the solution: a pivot below
+ *     2^-24 (times the plan's mass for entropic OT) makes the solve fail, and it
+ *     is repeated once with 2^-20 (mass + trace) added to the diagonal, which
+ *     fails only for a non-finite Delta (the solution is then taken as 0 and the
+ *     NaN stays in dH).  At an exact permutation (Delta = 0) the right-hand side
+ *     is exactly 0 as well, and the result is the exact dH = 0.
  *
  * Return codes: BIRKHOFF_OK or one of the negative BIRKHOFF_E* codes below;
  * birkhoff_strerror() describes them.
